@@ -1,0 +1,286 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+Each pin is chosen so that a plausible mistake in the oracle fails at least
+one of them: brute force over forward-simulated histories (catches a wrong
+lineage direction or index), torch's scaled_dot_product_attention in fp64 over
+keys gathered through the append oracle's slot tables (a third derivation of
+the key sequence), the exact split/merge identity, closed forms and
+invariants.
+"""
+import copy
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from generative_recommendation_beam_amd import inputs
+from generative_recommendation_beam_amd.inputs import Workload, make_workload, to_f64
+from oracle import attention as oa
+from oracle import append as oapp
+import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def tiny(seed, *, R=2, B=3, Hq=4, Hkv=2, D=8, P=(5, 0), L=(3, 2), dtype="f32", parent="uniform"):
+    return make_workload(f"tiny{seed}", R=R, B=B, Hq=Hq, Hkv=Hkv, D=D, prefix_len=list(P),
+                         unshared_len=list(L), dtype=dtype, seed_key=(100, seed),
+                         parent_dist=parent)
+
+
+TINY_CASES = [
+    dict(),
+    dict(P=(8, 3), L=(0, 3)),
+    dict(R=1, B=1, Hq=1, Hkv=1, P=(4,), L=(2,)),
+    dict(R=3, B=2, Hq=4, Hkv=1, P=(0, 1, 7), L=(1, 0, 3)),
+    dict(dtype="bf16", D=4, P=(6, 2), L=(2, 3)),
+    dict(R=1, B=3, Hq=2, Hkv=2, P=(0,), L=(0,)),
+]
+
+
+@pytest.mark.parametrize("i", range(len(TINY_CASES)))
+def test_oracle_matches_brute_force(i):
+    w = tiny(i, **TINY_CASES[i])
+    O, L = oa.attention(w)
+    Ob, Lb = brute.brute_attention(w)
+    np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
+    assert np.array_equal(np.isneginf(L), np.isneginf(Lb))
+    fin = np.isfinite(Lb)
+    np.testing.assert_allclose(L[fin], Lb[fin], rtol=0, atol=1e-12)
+
+
+def test_oracle_brute_force_all_lineages():
+    """Every parent assignment of B = 2 beams over 3 steps (16 lineage sets)."""
+    base = tiny(50, R=1, B=2, Hq=2, Hkv=1, D=4, P=(3,), L=(3,))
+    for p1, p2 in itertools.product(itertools.product(range(2), repeat=2), repeat=2):
+        w = copy.deepcopy(base)
+        w.parents[1] = p1
+        w.parents[2] = p2
+        O, L = oa.attention(w)
+        Ob, Lb = brute.brute_attention(w)
+        np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L, Lb, rtol=0, atol=1e-12)
+
+
+def _pool_and_table_via_append(w):
+    """Run the append oracle step by step; returns (k_pool, v_pool, table)."""
+    kpool = np.zeros((w.num_slots, w.Hkv, w.D))
+    vpool = np.zeros_like(kpool)
+    table = np.full((w.N_b, w.T_max), -1, dtype=np.int64)
+    ulen = np.zeros(w.R, dtype=np.int64)
+    for t in range(w.T_steps):
+        oapp.cache_append(B=w.B, k_new=to_f64(w.k_new[t]), v_new=to_f64(w.v_new[t]),
+                          parent=w.parents[t], slot_base=w.slot_base, active=w.active(t),
+                          k_pool=kpool, v_pool=vpool, table_in=table, table_out=table,
+                          unshared_len=ulen)
+    assert np.array_equal(ulen, w.unshared_len)
+    return kpool, vpool, table
+
+
+def _sdpa_reference(w, prefix=True, generated=True):
+    """torch SDPA in fp64 on CPU, one beam at a time, keys gathered via slots."""
+    kpool, vpool, table = _pool_and_table_via_append(w)
+    G = w.Hq // w.Hkv
+    Q, KS, VS = to_f64(w.q), to_f64(w.k_shared), to_f64(w.v_shared)
+    O = np.zeros((w.N_b, w.Hq, w.D))
+    for r in range(w.R):
+        off, P, L = int(w.prefix_off[r]), int(w.prefix_len[r]), int(w.unshared_len[r])
+        for b in range(w.B):
+            n = r * w.B + b
+            kk = [KS[:, off:off + P].transpose(1, 0, 2)] if prefix else []
+            vv = [VS[:, off:off + P].transpose(1, 0, 2)] if prefix else []
+            if generated:
+                kk.append(kpool[table[n, :L]])
+                vv.append(vpool[table[n, :L]])
+            k = torch.from_numpy(np.concatenate(kk, 0)).permute(1, 0, 2)  # [Hkv, S, D]
+            v = torch.from_numpy(np.concatenate(vv, 0)).permute(1, 0, 2)
+            k = k.repeat_interleave(G, dim=0)
+            v = v.repeat_interleave(G, dim=0)
+            q = torch.from_numpy(Q[n])[:, None, :]                       # [Hq, 1, D]
+            if k.shape[1] == 0:
+                continue
+            o = torch.nn.functional.scaled_dot_product_attention(
+                q, k, v, scale=float(np.float32(w.scale)))
+            O[n] = o[:, 0, :].numpy()
+    return O
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_oracle_matches_torch_sdpa_fp64(dtype):
+    w = make_workload("sdpa", R=3, B=4, Hq=8, Hkv=2, D=16, prefix_len=[40, 17, 0],
+                      unshared_len=[3, 1, 4], dtype=dtype, seed_key=(101, 0), qkv_std=1.5)
+    O, _ = oa.attention(w)
+    np.testing.assert_allclose(O, _sdpa_reference(w), rtol=0, atol=1e-10)
+    Os, _ = oa.attention(w, include_generated=False)   # Shared stage alone
+    ref = _sdpa_reference(w, generated=False)
+    nz = w.prefix_len[np.arange(w.N_b) // w.B] > 0
+    np.testing.assert_allclose(Os[nz], ref[nz], rtol=0, atol=1e-10)
+    Ou, _ = oa.attention(w, include_prefix=False)      # Non-Shared stage alone
+    np.testing.assert_allclose(Ou, _sdpa_reference(w, prefix=False), rtol=0, atol=1e-10)
+
+
+def test_closed_form_golden():
+    g = json.load(open(os.path.join(GOLDEN, "closed_form_attention.json")))
+    f = lambda a: np.asarray(a, dtype=np.float32)
+    w = Workload(name="golden", dtype="f32", R=1, B=1, Hq=1, Hkv=1, D=2,
+                 prefix_len=np.array([2], np.int32), prefix_off=np.array([0], np.int64),
+                 unshared_len=np.array([1], np.int32), T_max=1, scale=np.float32(1.0),
+                 q=f(g["q"]).reshape(1, 1, 2), k_shared=f(g["prefix_k"]).reshape(1, 2, 2),
+                 v_shared=f(g["prefix_v"]).reshape(1, 2, 2),
+                 k_new=f(g["gen_k"]).reshape(1, 1, 1, 2), v_new=f(g["gen_v"]).reshape(1, 1, 1, 2),
+                 parents=np.zeros((1, 1), np.int32), slot_base=np.zeros(1, np.int64), num_slots=1)
+    tol = g["tolerance"]
+    O, L = oa.attention(w)
+    np.testing.assert_allclose(O[0, 0], g["expect_o"], atol=tol)
+    assert abs(L[0, 0] - g["expect_lse"]) < tol
+    O, L = oa.attention(w, include_generated=False)
+    np.testing.assert_allclose(O[0, 0], g["expect_o_shared"], atol=tol)
+    assert abs(L[0, 0] - g["expect_lse_shared"]) < tol
+    O, L = oa.attention(w, include_prefix=False)
+    np.testing.assert_allclose(O[0, 0], g["expect_o_unshared"], atol=tol)
+    assert abs(L[0, 0] - g["expect_lse_unshared"]) < tol
+
+
+def test_merge_identity_two_stage():
+    """merge(Shared-only, Non-Shared-only) == attention over the concatenation."""
+    w = make_workload("m", R=3, B=5, Hq=6, Hkv=3, D=32, prefix_len=[100, 0, 33],
+                      unshared_len=[4, 2, 0], seed_key=(102, 0), qkv_std=2.0)
+    O, L = oa.attention(w)
+    Os, Ls = oa.attention(w, include_generated=False)
+    Ou, Lu = oa.attention(w, include_prefix=False)
+    Om, Lm = oa.merge(Os, Ls, Ou, Lu)
+    np.testing.assert_allclose(Om, O, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(Lm, L, rtol=0, atol=1e-12)
+
+
+def test_merge_identity_many_parts():
+    """n-part merge over arbitrary contiguous partitions of the prompt."""
+    w = make_workload("mp", R=1, B=3, Hq=4, Hkv=2, D=16, prefix_len=97, unshared_len=2,
+                      seed_key=(103, 0), qkv_std=2.0)
+    O, L = oa.attention(w)
+    cuts = [0, 1, 30, 31, 64, 97]
+    parts = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        ws = copy.copy(w)
+        ws.prefix_off = w.prefix_off + a
+        ws.prefix_len = np.array([b - a], np.int32)
+        parts.append(oa.attention(ws, include_generated=False))
+    parts.append(oa.attention(w, include_prefix=False))
+    rng = np.random.default_rng(0)
+    rng.shuffle(parts)                          # order independence
+    Om, Lm = oa.merge_many(parts)
+    np.testing.assert_allclose(Om, O, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(Lm, L, rtol=0, atol=1e-12)
+
+
+def test_merge_empty_parts():
+    o = np.random.default_rng(1).standard_normal((4, 8))
+    lse = np.array([0.3, -2.0, 5.0, 1.0])
+    ninf = np.full(4, -np.inf)
+    Om, Lm = oa.merge(o, lse, np.zeros((4, 8)), ninf)
+    np.testing.assert_array_equal(Om, o)
+    np.testing.assert_array_equal(Lm, lse)
+    Om, Lm = oa.merge(np.zeros((4, 8)), ninf, np.zeros((4, 8)), ninf)
+    assert np.all(Om == 0) and np.all(np.isneginf(Lm)) and not np.isnan(Om).any()
+
+
+def test_identical_histories_identical_outputs():
+    w = make_workload("ih", R=2, B=6, Hq=4, Hkv=2, D=16, prefix_len=[20, 9], unshared_len=[4, 3],
+                      seed_key=(104, 0))
+    r, b1, b2 = 1, 2, 5
+    n1, n2 = r * w.B + b1, r * w.B + b2
+    w.q[n2] = w.q[n1]
+    for t in range(w.T_steps):
+        w.parents[t, n2] = w.parents[t, n1]
+        w.k_new[t, n2] = w.k_new[t, n1]
+        w.v_new[t, n2] = w.v_new[t, n1]
+    O, L = oa.attention(w)
+    np.testing.assert_allclose(O[n2], O[n1], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(L[n2], L[n1], rtol=0, atol=1e-15)
+
+
+def test_beam_relabeling_permutes_outputs():
+    """Relabel beams by a permutation at every step; outputs follow."""
+    w = make_workload("perm", R=2, B=5, Hq=2, Hkv=1, D=8, prefix_len=[7, 3], unshared_len=[3, 4],
+                      seed_key=(105, 0))
+    perm = np.array([3, 0, 4, 1, 2])      # old beam b -> new label perm[b]
+    w2 = copy.deepcopy(w)
+    for r in range(w.R):
+        for b in range(w.B):
+            n, n2 = r * w.B + b, r * w.B + perm[b]
+            w2.q[n2] = w.q[n]
+            for t in range(w.T_steps):
+                w2.k_new[t, n2] = w.k_new[t, n]
+                w2.v_new[t, n2] = w.v_new[t, n]
+                w2.parents[t, n2] = perm[w.parents[t, n]]
+    O, L = oa.attention(w)
+    O2, L2 = oa.attention(w2)
+    for r in range(w.R):
+        for b in range(w.B):
+            np.testing.assert_allclose(O2[r * w.B + perm[b]], O[r * w.B + b], atol=1e-13)
+
+
+def test_beam_width_one_is_standard_decode():
+    w = make_workload("b1", R=1, B=1, Hq=4, Hkv=2, D=8, prefix_len=11, unshared_len=5,
+                      seed_key=(106, 0), parent_dist="identity")
+    G = 2
+    O, L = oa.attention(w)
+    K = np.concatenate([to_f64(w.k_shared)[:, :11], to_f64(w.k_new)[:, 0].transpose(1, 0, 2)], 1)
+    V = np.concatenate([to_f64(w.v_shared)[:, :11], to_f64(w.v_new)[:, 0].transpose(1, 0, 2)], 1)
+    q = to_f64(w.q)[0]
+    for qh in range(4):
+        s = float(np.float32(w.scale)) * K[qh // G] @ q[qh]
+        p = np.exp(s - s.max())
+        np.testing.assert_allclose(O[0, qh], p @ V[qh // G] / p.sum(), atol=1e-13)
+        assert abs(L[0, qh] - (s.max() + np.log(p.sum()))) < 1e-13
+
+
+def test_constant_v_gives_v():
+    w = make_workload("cv", R=2, B=3, Hq=4, Hkv=2, D=8, prefix_len=[9, 0], unshared_len=[2, 3],
+                      dtype="f32", seed_key=(107, 0), qkv_std=3.0)
+    c = np.arange(8, dtype=np.float32) - 3.5
+    w.v_shared[:] = c
+    w.v_new[:] = c
+    O, _ = oa.attention(w)
+    np.testing.assert_allclose(O, np.broadcast_to(c, O.shape), atol=1e-12)
+
+
+def test_constant_k_gives_mean_v():
+    w = make_workload("ck", R=2, B=3, Hq=4, Hkv=2, D=8, prefix_len=[9, 4], unshared_len=[2, 3],
+                      dtype="f32", seed_key=(108, 0))
+    w.k_shared[:] = 0.25
+    w.k_new[:] = 0.25
+    O, L = oa.attention(w)
+    G = 2
+    for r in range(w.R):
+        for b in range(w.B):
+            for qh in range(w.Hq):
+                ks, vs = brute.beam_keys(w, r, b, qh // G)
+                np.testing.assert_allclose(O[r * w.B + b, qh], np.mean(vs, axis=0), atol=1e-12)
+                s = float(np.float32(w.scale)) * 0.25 * to_f64(w.q)[r * w.B + b, qh].sum()
+                assert abs(L[r * w.B + b, qh] - (s + math.log(len(ks)))) < 1e-12
+
+
+def test_attention_rows_matches_full():
+    w = make_workload("rows", R=2, B=4, Hq=8, Hkv=2, D=16, prefix_len=[30, 12], unshared_len=[3, 2],
+                      seed_key=(109, 0), parent_dist="zipf")
+    O, L = oa.attention(w)
+    rows = [(0, 0), (3, 7), (5, 2), (7, 5)]
+    Or, Lr = oa.attention_rows(w, rows)
+    for i, (n, q) in enumerate(rows):
+        np.testing.assert_allclose(Or[i], O[n, q], atol=1e-13)
+        assert abs(Lr[i] - L[n, q]) < 1e-13
+
+
+def test_prefix_homogeneous_equals_distinct_prefixes():
+    a = make_workload("4a-mini", R=2, B=3, Hq=4, Hkv=2, D=16, prefix_len=21, unshared_len=4,
+                      seed_key=(110, 0), parent_dist="identity")
+    b = inputs.as_distinct_prefixes(a, "4b-mini")
+    Oa, La = oa.attention(a)
+    Ob, Lb = oa.attention(b)
+    np.testing.assert_allclose(Oa, Ob, atol=1e-13)
+    np.testing.assert_allclose(La, Lb, atol=1e-13)
