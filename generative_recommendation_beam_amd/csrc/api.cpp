@@ -1,0 +1,400 @@
+// C-ABI entry points: host-side validation, launch planning, workspace
+// layout and dispatch. Nothing is enqueued unless every host-checkable
+// argument is valid. The library never allocates, frees or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "../../include/xattn.h"
+#include "kernels.h"
+
+using namespace xattn;
+
+namespace {
+
+constexpr int kMaxBeamWidth = 16384;   // one request's table chunk must fit in LDS
+constexpr int kTargetWaves = 2048;     // enough resident waves to cover 256 CUs
+constexpr int kMinSplitKeys = 256;     // never split the prompt finer than this
+constexpr int kFuseMaxUnshared = 16;   // T_max up to this: Non-Shared part in the epilogue
+constexpr int kUnsharedChunk = 64;     // generated tokens per Non-Shared split
+constexpr int kMfmaMinRows = 16;       // fewer query rows per (r,h): vector path
+
+struct Plan {
+  int mfma;
+  int waves;
+  int row_tiles;
+  int p_splits;
+  int p_chunk;
+  int u_splits;  // 0 = fused into the prompt pass (or absent)
+  int u_chunk;
+  int parts;
+  int ngroups;   // vector path: query-head groups per (beam, kv head)
+};
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// K/V buffers of an empty cache (no prompt tokens / no pool slots) may be NULL.
+bool kv_ok(const void* k, const void* v, int64_t extent) {
+  if (extent == 0) return (!k || aligned16(k)) && (!v || aligned16(v));
+  return k && v && aligned16(k) && aligned16(v);
+}
+
+xattn_status check_dims(const xattn_dims* d) {
+  if (!d) return XATTN_ERR_INVALID_ARG;
+  if (d->num_requests < 0 || d->beam_width < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1)
+    return XATTN_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return XATTN_ERR_INVALID_ARG;
+  if (d->max_prefix_len < 0 || d->max_unshared_len < 1 || d->num_slots < 0 ||
+      d->num_prefix_tokens < 0)
+    return XATTN_ERR_INVALID_ARG;
+  if (d->prefix_splits < 0 || d->unshared_splits < 0) return XATTN_ERR_INVALID_ARG;
+  if (!(d->scale == d->scale)) return XATTN_ERR_INVALID_ARG;  // NaN
+  if (d->head_dim != 64 && d->head_dim != 128) return XATTN_ERR_UNSUPPORTED;
+  if (d->dtype != XATTN_F32 && d->dtype != XATTN_BF16) return XATTN_ERR_UNSUPPORTED;
+  if (d->beam_width > kMaxBeamWidth) return XATTN_ERR_UNSUPPORTED;
+  const int64_t nb = (int64_t)d->num_requests * d->beam_width;
+  if (nb * d->num_q_heads > (int64_t)INT32_MAX) return XATTN_ERR_UNSUPPORTED;
+  return XATTN_OK;
+}
+
+// which: 0 shared stage, 1 unshared stage, 2 decode
+Plan make_plan(const xattn_dims* d, int which) {
+  Plan p{};
+  const int G = d->num_q_heads / d->num_kv_heads;
+  const int64_t M = (int64_t)d->beam_width * G;
+  const int64_t N_b = (int64_t)d->num_requests * d->beam_width;
+  const int maxP = d->max_prefix_len;
+  const int T = d->max_unshared_len;
+  p.mfma = (d->dtype == XATTN_BF16 && M >= kMfmaMinRows) ? 1 : 0;
+  {
+    const int NG = (G >= 8 || (G & (G - 1))) ? 8 : G;
+    p.ngroups = (G + NG - 1) / NG;
+  }
+  const bool want_prefix = which != 1;
+  const bool want_gen = which != 0;
+
+  p.p_splits = 1;
+  p.p_chunk = std::max(64, (int)cdiv(std::max(maxP, 1), 64) * 64);
+  if (want_prefix) {
+    int64_t base_waves;
+    if (p.mfma) {
+      p.waves = M >= 128 ? 4 : (M > 32 ? 2 : 1);
+      p.row_tiles = (int)cdiv(M, 32 * p.waves);
+      base_waves = (int64_t)d->num_requests * d->num_kv_heads * p.row_tiles * p.waves;
+    } else {
+      p.waves = 1;
+      p.row_tiles = 1;
+      base_waves = N_b * d->num_kv_heads * p.ngroups;
+    }
+    int s;
+    if (d->prefix_splits > 0) {
+      s = d->prefix_splits;
+    } else {
+      s = base_waves > 0 ? (int)cdiv(kTargetWaves, base_waves) : 1;
+      s = (int)std::min<int64_t>(s, std::max<int64_t>(1, cdiv(maxP, kMinSplitKeys)));
+      s = std::max(s, 1);
+    }
+    p.p_chunk = std::max(64, (int)cdiv(cdiv(std::max(maxP, 1), s), 64) * 64);
+    p.p_splits = std::max(1, (int)cdiv(std::max(maxP, 1), p.p_chunk));
+    if (d->prefix_splits > 0) p.p_splits = std::max(p.p_splits, 1);
+  }
+  p.u_splits = 0;
+  p.u_chunk = T;
+  if (want_gen) {
+    if (which == 1) {
+      // Non-Shared stage alone: split only long generated tails.
+      const int s = d->unshared_splits > 0 ? d->unshared_splits
+                                           : (T > 4 * kUnsharedChunk ? (int)cdiv(T, kUnsharedChunk) : 1);
+      p.u_chunk = (int)cdiv(T, s);
+      p.u_splits = (int)cdiv(T, p.u_chunk);
+    } else {
+      // decode: fuse into the prompt pass when short and not forced apart
+      const bool fuse = d->unshared_splits == 0 && T <= kFuseMaxUnshared &&
+                        (p.mfma || p.p_splits == 1);
+      if (!fuse) {
+        const int s = d->unshared_splits > 0 ? d->unshared_splits : (int)cdiv(T, kUnsharedChunk);
+        p.u_chunk = (int)cdiv(T, s);
+        p.u_splits = (int)cdiv(T, p.u_chunk);
+      }
+    }
+  }
+  if (which == 0) p.parts = p.p_splits > 1 ? p.p_splits : 0;
+  else if (which == 1) p.parts = p.u_splits > 1 ? p.u_splits : 0;
+  else p.parts = (p.p_splits > 1 || p.u_splits > 0) ? p.p_splits + p.u_splits : 0;
+  return p;
+}
+
+size_t ws_bytes_for(const xattn_dims* d, const Plan& p) {
+  if (p.parts == 0) return 0;
+  const int64_t rows = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
+  const size_t o = (size_t)p.parts * rows * d->head_dim * sizeof(float);
+  const size_t l = (size_t)p.parts * rows * sizeof(float);
+  return ((o + 255) / 256) * 256 + ((l + 255) / 256) * 256;
+}
+
+Shape make_shape(const xattn_dims* d) {
+  Shape s;
+  s.R = d->num_requests;
+  s.B = d->beam_width;
+  s.Hq = d->num_q_heads;
+  s.Hkv = d->num_kv_heads;
+  s.D = d->head_dim;
+  s.T_max = d->max_unshared_len;
+  s.n_ptok = d->num_prefix_tokens;
+  s.scale_log2 = d->scale * 1.4426950408889634f;
+  return s;
+}
+
+struct Workspace {
+  float* o;
+  float* lse;
+};
+
+Workspace carve(const xattn_dims* d, const Plan& p, void* ws) {
+  const int64_t rows = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
+  const size_t o = (size_t)p.parts * rows * d->head_dim * sizeof(float);
+  Workspace w;
+  w.o = static_cast<float*>(ws);
+  w.lse = reinterpret_cast<float*>(static_cast<char*>(ws) + ((o + 255) / 256) * 256);
+  return w;
+}
+
+inline xattn_status hip_status(hipError_t e) { return e == hipSuccess ? XATTN_OK : XATTN_ERR_HIP; }
+
+// Launch the prompt pass (MFMA or vector) into `out`, with optional fused
+// Non-Shared epilogue pointers.
+hipError_t run_prefix(const xattn_dims* d, const Plan& p, const void* q, const void* ks,
+                      const void* vs, const int64_t* poff, const int32_t* plen, const void* kp,
+                      const void* vp, const int32_t* table, const int32_t* ulen, OutSpec out,
+                      hipStream_t st) {
+  if (p.mfma) {
+    SharedMfmaArgs a;
+    a.s = make_shape(d);
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_shared = static_cast<const uint16_t*>(ks);
+    a.v_shared = static_cast<const uint16_t*>(vs);
+    a.prefix_off = poff;
+    a.prefix_len = plen;
+    a.k_pool = static_cast<const uint16_t*>(kp);
+    a.v_pool = static_cast<const uint16_t*>(vp);
+    a.slot_table = table;
+    a.unshared_len = ulen;
+    a.out = out;
+    a.waves = p.waves;
+    a.row_tiles = p.row_tiles;
+    a.p_splits = p.p_splits;
+    a.p_chunk = p.p_chunk;
+    return launch_shared_mfma(a, st);
+  }
+  ValuArgs a;
+  a.s = make_shape(d);
+  a.dtype = d->dtype;
+  a.q = q;
+  a.k_shared = ks;
+  a.v_shared = vs;
+  a.prefix_off = poff;
+  a.prefix_len = plen;
+  a.k_pool = kp;
+  a.v_pool = vp;
+  a.slot_table = table;
+  a.unshared_len = ulen;
+  a.use_prefix = 1;
+  a.use_gen = kp != nullptr ? 1 : 0;
+  a.splits = p.p_splits;
+  a.chunk = p.p_chunk;
+  a.out = out;
+  return launch_valu_attn(a, st);
+}
+
+hipError_t run_gen(const xattn_dims* d, const Plan& p, const void* q, const void* kp,
+                   const void* vp, const int32_t* table, const int32_t* ulen, OutSpec out,
+                   hipStream_t st) {
+  ValuArgs a;
+  a.s = make_shape(d);
+  a.dtype = d->dtype;
+  a.q = q;
+  a.k_shared = nullptr;
+  a.v_shared = nullptr;
+  a.prefix_off = nullptr;
+  a.prefix_len = nullptr;
+  a.k_pool = kp;
+  a.v_pool = vp;
+  a.slot_table = table;
+  a.unshared_len = ulen;
+  a.use_prefix = 0;
+  a.use_gen = 1;
+  a.splits = std::max(1, p.u_splits);
+  a.chunk = p.u_chunk;
+  a.out = out;
+  return launch_valu_attn(a, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* xattn_status_string(xattn_status s) {
+  switch (s) {
+    case XATTN_OK: return "XATTN_OK";
+    case XATTN_ERR_INVALID_ARG: return "XATTN_ERR_INVALID_ARG: invalid argument";
+    case XATTN_ERR_UNSUPPORTED: return "XATTN_ERR_UNSUPPORTED: shape or dtype not supported";
+    case XATTN_ERR_WORKSPACE: return "XATTN_ERR_WORKSPACE: workspace missing or too small";
+    case XATTN_ERR_HIP: return "XATTN_ERR_HIP: HIP launch error";
+  }
+  return "XATTN_UNKNOWN_STATUS";
+}
+
+xattn_status xattn_get_plan(const xattn_dims* d, int which, xattn_plan* out) {
+  xattn_status e = check_dims(d);
+  if (e != XATTN_OK) return e;
+  if (!out || which < 0 || which > 2) return XATTN_ERR_INVALID_ARG;
+  const Plan p = make_plan(d, which);
+  out->rows_per_block = p.mfma ? 32 * p.waves : 0;
+  out->row_tiles = p.mfma ? p.row_tiles : 0;
+  out->prefix_splits = which == 1 ? 0 : p.p_splits;
+  out->prefix_chunk = which == 1 ? 0 : p.p_chunk;
+  out->unshared_splits = p.u_splits;
+  out->unshared_chunk = which == 0 ? 0 : p.u_chunk;
+  out->partials = p.parts;
+  out->mfma = p.mfma;
+  return XATTN_OK;
+}
+
+xattn_status xattn_workspace_size(const xattn_dims* d, int which, size_t* bytes) {
+  xattn_status e = check_dims(d);
+  if (e != XATTN_OK) return e;
+  if (!bytes || which < 0 || which > 2) return XATTN_ERR_INVALID_ARG;
+  *bytes = ws_bytes_for(d, make_plan(d, which));
+  return XATTN_OK;
+}
+
+xattn_status xattn_shared_stage(const xattn_dims* d, const void* q, const void* ks, const void* vs,
+                                const int64_t* poff, const int32_t* plen, float* o, float* lse,
+                                void* ws, size_t ws_bytes, void* stream) {
+  xattn_status e = check_dims(d);
+  if (e != XATTN_OK) return e;
+  if (!q || !poff || !plen || !o || !lse) return XATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(o) || !kv_ok(ks, vs, d->num_prefix_tokens))
+    return XATTN_ERR_INVALID_ARG;
+  const Plan p = make_plan(d, 0);
+  const size_t need = ws_bytes_for(d, p);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return XATTN_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t rows = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
+  if (p.parts == 0) {
+    return hip_status(run_prefix(d, p, q, ks, vs, poff, plen, nullptr, nullptr, nullptr, nullptr,
+                                 OutSpec{o, lse, 0, 0}, st));
+  }
+  Workspace w = carve(d, p, ws);
+  hipError_t he = run_prefix(d, p, q, ks, vs, poff, plen, nullptr, nullptr, nullptr, nullptr,
+                             OutSpec{w.o, w.lse, rows, 0}, st);
+  if (he != hipSuccess) return XATTN_ERR_HIP;
+  return hip_status(launch_merge_parts(rows, d->head_dim, p.parts, w.o, w.lse, o, lse, st));
+}
+
+xattn_status xattn_unshared_stage(const xattn_dims* d, const void* q, const void* kp,
+                                  const void* vp, const int32_t* table, const int32_t* ulen,
+                                  float* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  xattn_status e = check_dims(d);
+  if (e != XATTN_OK) return e;
+  if (!q || !table || !ulen || !o || !lse) return XATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(o) || !kv_ok(kp, vp, d->num_slots)) return XATTN_ERR_INVALID_ARG;
+  const Plan p = make_plan(d, 1);
+  const size_t need = ws_bytes_for(d, p);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return XATTN_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t rows = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
+  if (p.parts == 0) {
+    Plan p1 = p;
+    p1.u_splits = 1;
+    return hip_status(run_gen(d, p1, q, kp, vp, table, ulen, OutSpec{o, lse, 0, 0}, st));
+  }
+  Workspace w = carve(d, p, ws);
+  hipError_t he = run_gen(d, p, q, kp, vp, table, ulen, OutSpec{w.o, w.lse, rows, 0}, st);
+  if (he != hipSuccess) return XATTN_ERR_HIP;
+  return hip_status(launch_merge_parts(rows, d->head_dim, p.parts, w.o, w.lse, o, lse, st));
+}
+
+xattn_status xattn_merge(int64_t rows, int32_t head_dim, const float* o_a, const float* lse_a,
+                         const float* o_b, const float* lse_b, float* o_out, float* lse_out,
+                         void* stream) {
+  if (rows < 0 || head_dim <= 0) return XATTN_ERR_INVALID_ARG;
+  // a row's threads (head_dim / 4 of them) must tile a 256-thread block
+  if (head_dim % 4 != 0 || 256 % (head_dim / 4) != 0) return XATTN_ERR_UNSUPPORTED;
+  if (rows == 0) return XATTN_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o_out) return XATTN_ERR_INVALID_ARG;
+  if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o_out)) return XATTN_ERR_INVALID_ARG;
+  return hip_status(launch_merge2(rows, head_dim, o_a, lse_a, o_b, lse_b, o_out, lse_out,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+xattn_status xattn_decode(const xattn_dims* d, const void* q, const void* ks, const void* vs,
+                          const int64_t* poff, const int32_t* plen, const void* kp, const void* vp,
+                          const int32_t* table, const int32_t* ulen, float* o, float* lse,
+                          void* ws, size_t ws_bytes, void* stream) {
+  xattn_status e = check_dims(d);
+  if (e != XATTN_OK) return e;
+  if (!q || !poff || !plen || !table || !ulen || !o) return XATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(o) || !kv_ok(ks, vs, d->num_prefix_tokens) ||
+      !kv_ok(kp, vp, d->num_slots))
+    return XATTN_ERR_INVALID_ARG;
+  const Plan p = make_plan(d, 2);
+  const size_t need = ws_bytes_for(d, p);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return XATTN_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t rows = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
+  const bool fused = p.u_splits == 0;
+  if (p.parts == 0) {
+    // one launch: prompt pass with the Non-Shared tokens folded into its epilogue
+    return hip_status(run_prefix(d, p, q, ks, vs, poff, plen, kp, vp, table, ulen,
+                                 OutSpec{o, lse, 0, 0}, st));
+  }
+  Workspace w = carve(d, p, ws);
+  hipError_t he = run_prefix(d, p, q, ks, vs, poff, plen, fused ? kp : nullptr,
+                             fused ? vp : nullptr, table, ulen, OutSpec{w.o, w.lse, rows, 0}, st);
+  if (he != hipSuccess) return XATTN_ERR_HIP;
+  if (!fused) {
+    he = run_gen(d, p, q, kp, vp, table, ulen, OutSpec{w.o, w.lse, rows, p.p_splits}, st);
+    if (he != hipSuccess) return XATTN_ERR_HIP;
+  }
+  return hip_status(launch_merge_parts(rows, d->head_dim, p.parts, w.o, w.lse, o, lse, st));
+}
+
+xattn_status xattn_cache_append(const xattn_dims* d, const void* k_new, const void* v_new,
+                                const int32_t* parent, const int64_t* slot_base,
+                                const uint8_t* active, void* k_pool, void* v_pool,
+                                const int32_t* table_in, int32_t* table_out, int32_t* ulen,
+                                void* stream) {
+  xattn_status e = check_dims(d);
+  if (e != XATTN_OK) return e;
+  if (!k_new || !v_new || !parent || !slot_base || !k_pool || !v_pool || !table_in ||
+      !table_out || !ulen)
+    return XATTN_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return XATTN_ERR_INVALID_ARG;
+  const int64_t N_b = (int64_t)d->num_requests * d->beam_width;
+  if (d->num_requests > 0 && d->num_slots < N_b) return XATTN_ERR_INVALID_ARG;
+  AppendArgs a;
+  a.R = d->num_requests;
+  a.B = d->beam_width;
+  a.Hkv = d->num_kv_heads;
+  a.D = d->head_dim;
+  a.T_max = d->max_unshared_len;
+  a.elem_bytes = d->dtype == XATTN_BF16 ? 2 : 4;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.parent = parent;
+  a.slot_base = slot_base;
+  a.active = active;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.table_in = table_in;
+  a.table_out = table_out;
+  a.unshared_len = ulen;
+  return hip_status(launch_append(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Kernel parameter blocks and host launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xattn {
+
+// Where a stage writes: the final outputs, or partial slot `part` of the
+// workspace (partials are [parts][N_b*H_q][D] and [parts][N_b*H_q]).
+struct OutSpec {
+  float* o;
+  float* lse;           // may be null for final outputs
+  int64_t part_stride;  // rows between partial slots (N_b*H_q); 0 for final
+  int part_base;        // first partial slot this launch writes
+};
+
+struct Shape {
+  int R, B, Hq, Hkv, D, T_max;
+  int64_t n_ptok;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+// ---- Shared stage, bf16 MFMA (shared_mfma.hip) ----
+struct SharedMfmaArgs {
+  Shape s;
+  const uint16_t* q;
+  const uint16_t* k_shared;
+  const uint16_t* v_shared;
+  const int64_t* prefix_off;
+  const int32_t* prefix_len;
+  // Non-Shared part folded into the epilogue of prefix split 0 (null = none)
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* slot_table;
+  const int32_t* unshared_len;
+  OutSpec out;
+  int waves;        // waves per block: 1, 2 or 4 (32 query rows each)
+  int row_tiles;
+  int p_splits;
+  int p_chunk;      // multiple of 64
+};
+hipError_t launch_shared_mfma(const SharedMfmaArgs& a, hipStream_t st);
+
+// ---- Vector-ALU attention over prompt and/or generated keys (valu_attn.hip) ----
+struct ValuArgs {
+  Shape s;
+  int dtype;  // 0 f32, 1 bf16 (storage of q and K/V)
+  const void* q;
+  const void* k_shared;
+  const void* v_shared;
+  const int64_t* prefix_off;
+  const int32_t* prefix_len;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* slot_table;
+  const int32_t* unshared_len;
+  int use_prefix, use_gen;
+  int splits;       // key-range splits (over the prompt if use_prefix, else over generated)
+  int chunk;        // keys per split
+  OutSpec out;      // writes slot part_base + split when out.part_stride != 0
+};
+hipError_t launch_valu_attn(const ValuArgs& a, hipStream_t st);
+
+// ---- Merge (merge.hip) ----
+hipError_t launch_merge2(int64_t rows, int D, const float* o_a, const float* lse_a, const float* o_b,
+                         const float* lse_b, float* o_out, float* lse_out, hipStream_t st);
+// Reduce `parts` partial slots [parts][rows][D] into final o/lse (lse nullable).
+hipError_t launch_merge_parts(int64_t rows, int D, int parts, const float* po, const float* plse,
+                              float* o, float* lse, hipStream_t st);
+
+// ---- Append (append.hip) ----
+struct AppendArgs {
+  int R, B, Hkv, D, T_max, elem_bytes;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* parent;
+  const int64_t* slot_base;
+  const uint8_t* active;
+  void* k_pool;
+  void* v_pool;
+  const int32_t* table_in;
+  int32_t* table_out;
+  int32_t* unshared_len;
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+
+}  // namespace xattn

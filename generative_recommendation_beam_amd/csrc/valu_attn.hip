@@ -1,0 +1,231 @@
+// Vector-ALU attention of a few query rows over a key range (no MFMA).
+//
+// Used for the Non-Shared stage (xGR page, section 2.1 xAttention: each beam
+// attends to its own generated tokens, gathered through its slot-table row
+// from the token-granular pool), for the fp32 path, and for the Shared stage
+// when a (request, kv head) has too few query rows to fill an MFMA tile.
+// The Non-Shared work is bandwidth-bound and tiny per beam: a GEMV, not a
+// contraction worth the matrix cores.
+//
+// One wavefront owns one unit = (beam n, kv head h, group of up to NG query
+// heads of that kv head, key split). Its 64 lanes form 4 key slots of 16
+// lanes; a slot's 16 lanes hold one key row (D/16 elements each), so a key
+// costs one 16-lane shuffle reduction per query row. Each slot keeps its own
+// online-softmax state (max, sum, output) over the keys it saw; the 4 slots
+// are combined at the end with the same log-sum-exp rule as the Merge stage.
+#include "device.h"
+#include "kernels.h"
+
+namespace xattn {
+
+namespace {
+
+constexpr int kValuWaves = 4;
+
+template <typename T, int D, int NG>
+struct ValuState {
+  static constexpr int EPL = D / 16;
+  float q[NG][EPL];
+  float m[NG], l[NG];
+  float acc[NG][EPL];
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      m[g] = neg_inf();
+      l[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+    }
+  }
+
+  // One step over the 4 keys held by the 4 slots. krow / vrow point to this
+  // lane's D/16 elements of its slot's key; `valid` is uniform per slot.
+  __device__ __forceinline__ void step(const T* krow, const T* vrow, bool valid) {
+    float kv[EPL], vv[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) kv[e] = vv[e] = 0.f;
+    if (valid) {
+      Load<T, EPL>::run(krow, kv);
+      Load<T, EPL>::run(vrow, vv);
+    }
+    float s[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a += q[g][e] * kv[e];
+      s[g] = a;
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) s[g] += __shfl_xor(s[g], off);
+    }
+    if (valid) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const float mn = fmaxf(m[g], s[g]);
+        const float alpha = exp2_approx(m[g] - mn);  // m = -inf -> 0
+        const float p = exp2_approx(s[g] - mn);
+        l[g] = l[g] * alpha + p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = acc[g][e] * alpha + p * vv[e];
+        m[g] = mn;
+      }
+    }
+  }
+
+  // Combine the 4 key slots (lanes 16 and 32 apart).
+  __device__ __forceinline__ void combine_slots() {
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const float mo = __shfl_xor(m[g], off);
+        const float lo = __shfl_xor(l[g], off);
+        const float mn = fmaxf(m[g], mo);
+        const float a1 = (m[g] == neg_inf()) ? 0.f : exp2_approx(m[g] - mn);
+        const float a2 = (mo == neg_inf()) ? 0.f : exp2_approx(mo - mn);
+        l[g] = l[g] * a1 + lo * a2;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float ao = __shfl_xor(acc[g][e], off);
+          acc[g][e] = acc[g][e] * a1 + ao * a2;
+        }
+        m[g] = mn;
+      }
+    }
+  }
+};
+
+template <typename T, int D, int NG>
+__global__ __launch_bounds__(kValuWaves * 64) void valu_attn_kernel(ValuArgs a, int64_t n_units,
+                                                                    int ngroups) {
+  constexpr int EPL = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = (int64_t)blockIdx.x * kValuWaves + (threadIdx.x >> 6);
+  if (unit >= n_units) return;  // uniform per wavefront
+  const Shape& s = a.s;
+  int64_t u = unit;
+  const int split = (int)(u % a.splits);
+  u /= a.splits;
+  const int grp = (int)(u % ngroups);
+  u /= ngroups;
+  const int h = (int)(u % s.Hkv);
+  const int64_t n = u / s.Hkv;
+  const int r = (int)(n / s.B);
+  const int G = s.Hq / s.Hkv;
+  const int g0 = grp * NG;
+  const int ng = min(NG, G - g0);
+  const int slot_id = lane >> 4;
+  const int dl = lane & 15;
+
+  ValuState<T, D, NG> st;
+  st.init();
+  {
+    const T* qb = static_cast<const T*>(a.q) + ((n * s.Hq) + h * G + g0) * (int64_t)D + dl * EPL;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float tmp[EPL];
+      if (g < ng) {
+        Load<T, EPL>::run(qb + (int64_t)g * D, tmp);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) tmp[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) st.q[g][e] = tmp[e] * s.scale_log2;
+    }
+  }
+
+  if (a.use_prefix) {
+    const int P = a.prefix_len[r];
+    int k0 = 0, k1 = P;
+    if (!a.use_gen || a.splits > 1) {
+      k0 = split * a.chunk;
+      k1 = min(P, k0 + a.chunk);
+    }
+    const T* kb = static_cast<const T*>(a.k_shared) + ((int64_t)h * s.n_ptok + a.prefix_off[r]) * D + dl * EPL;
+    const T* vb = static_cast<const T*>(a.v_shared) + ((int64_t)h * s.n_ptok + a.prefix_off[r]) * D + dl * EPL;
+    for (int j0 = k0; j0 < k1; j0 += 4) {
+      const int j = j0 + slot_id;
+      const bool valid = j < k1;
+      const int jj = valid ? j : k0;
+      st.step(kb + (int64_t)jj * D, vb + (int64_t)jj * D, valid);
+    }
+  }
+  if (a.use_gen) {
+    const int L = a.unshared_len[r];
+    int t0 = 0, t1 = L;
+    if (!a.use_prefix) {
+      t0 = split * a.chunk;
+      t1 = min(L, t0 + a.chunk);
+    }
+    const int32_t* trow = a.slot_table + n * s.T_max;
+    const T* kp = static_cast<const T*>(a.k_pool);
+    const T* vp = static_cast<const T*>(a.v_pool);
+    for (int j0 = t0; j0 < t1; j0 += 4) {
+      const int j = j0 + slot_id;
+      const bool valid = j < t1;
+      const int64_t slot = valid ? (int64_t)trow[j] : 0;
+      const int64_t off = (slot * s.Hkv + h) * D + dl * EPL;
+      st.step(kp + off, vp + off, valid);
+    }
+  }
+  st.combine_slots();
+
+  if (slot_id != 0) return;
+  const int64_t row0 = n * s.Hq + h * G + g0;
+  float* ob = a.out.o;
+  float* lb = a.out.lse;
+  if (a.out.part_stride) {
+    const int64_t part = a.out.part_base + split;
+    ob += part * a.out.part_stride * D;
+    lb += part * a.out.part_stride;
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (g >= ng) break;
+    const float l = st.l[g];
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    float* dst = ob + (row0 + g) * D + dl * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4)
+      *reinterpret_cast<float4*>(dst + e) =
+          make_float4(st.acc[g][e] * inv, st.acc[g][e + 1] * inv, st.acc[g][e + 2] * inv,
+                      st.acc[g][e + 3] * inv);
+    if (lb && dl == 0) lb[row0 + g] = l > 0.f ? (st.m[g] + log2_approx(l)) * kLn2 : neg_inf();
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const ValuArgs& a, hipStream_t st) {
+  const int G = a.s.Hq / a.s.Hkv;
+  const int64_t N_b = (int64_t)a.s.R * a.s.B;
+  int NG = (G >= 8) ? 8 : (G >= 4 ? 4 : (G >= 2 ? 2 : 1));
+  if (G < 8 && (G & (G - 1))) NG = 8;  // non power of two: one masked group
+  const int ngroups = (G + NG - 1) / NG;
+  const int64_t units = N_b * a.s.Hkv * ngroups * a.splits;
+  if (units == 0) return hipSuccess;
+  const int64_t blocks = (units + kValuWaves - 1) / kValuWaves;
+  dim3 grid((unsigned)blocks), block(kValuWaves * 64);
+  switch (NG) {
+    case 1: hipLaunchKernelGGL((valu_attn_kernel<T, D, 1>), grid, block, 0, st, a, units, ngroups); break;
+    case 2: hipLaunchKernelGGL((valu_attn_kernel<T, D, 2>), grid, block, 0, st, a, units, ngroups); break;
+    case 4: hipLaunchKernelGGL((valu_attn_kernel<T, D, 4>), grid, block, 0, st, a, units, ngroups); break;
+    default: hipLaunchKernelGGL((valu_attn_kernel<T, D, 8>), grid, block, 0, st, a, units, ngroups); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_valu_attn(const ValuArgs& a, hipStream_t st) {
+  if (a.dtype == 1) {
+    return a.s.D == 64 ? launch_typed<uint16_t, 64>(a, st) : launch_typed<uint16_t, 128>(a, st);
+  }
+  return a.s.D == 64 ? launch_typed<float, 64>(a, st) : launch_typed<float, 128>(a, st);
+}
+
+}  // namespace xattn

@@ -1,0 +1,169 @@
+"""ctypes binding of the xattn C-ABI (argument marshalling only).
+
+Every step of the path runs in the HIP library ``libxattn.so``; this module
+only turns torch tensors into device pointers, passes the current HIP stream
+and raises on a non-OK status. If the library is missing, importing the
+binding's functions raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libxattn.so")
+
+XATTN_OK, XATTN_ERR_INVALID_ARG, XATTN_ERR_UNSUPPORTED, XATTN_ERR_WORKSPACE, XATTN_ERR_HIP = range(5)
+XATTN_F32, XATTN_BF16 = 0, 1
+
+EXPORTED = ("xattn_workspace_size", "xattn_get_plan", "xattn_shared_stage", "xattn_unshared_stage",
+            "xattn_merge", "xattn_decode", "xattn_cache_append", "xattn_status_string")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("num_requests", ctypes.c_int32), ("beam_width", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_prefix_len", ctypes.c_int32),
+                ("max_unshared_len", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("num_slots", ctypes.c_int64), ("num_prefix_tokens", ctypes.c_int64),
+                ("scale", ctypes.c_float), ("prefix_splits", ctypes.c_int32),
+                ("unshared_splits", ctypes.c_int32)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("rows_per_block", ctypes.c_int32), ("row_tiles", ctypes.c_int32),
+                ("prefix_splits", ctypes.c_int32), ("prefix_chunk", ctypes.c_int32),
+                ("unshared_splits", ctypes.c_int32), ("unshared_chunk", ctypes.c_int32),
+                ("partials", ctypes.c_int32), ("mfma", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class XattnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+_lib = None
+
+
+def lib():
+    """Load libxattn.so (built in-tree); raise loudly if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"xattn HIP library not built: {LIB_PATH} is missing "
+                           "(run __graft_entry__.build() or python -m "
+                           "generative_recommendation_beam_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    pd = ctypes.POINTER(Dims)
+    L.xattn_status_string.restype = ctypes.c_char_p
+    L.xattn_status_string.argtypes = [ctypes.c_int]
+    L.xattn_workspace_size.restype = ctypes.c_int
+    L.xattn_workspace_size.argtypes = [pd, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    L.xattn_get_plan.restype = ctypes.c_int
+    L.xattn_get_plan.argtypes = [pd, ctypes.c_int, ctypes.POINTER(Plan)]
+    L.xattn_shared_stage.restype = ctypes.c_int
+    L.xattn_shared_stage.argtypes = [pd, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.xattn_unshared_stage.restype = ctypes.c_int
+    L.xattn_unshared_stage.argtypes = [pd, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.xattn_merge.restype = ctypes.c_int
+    L.xattn_merge.argtypes = [ctypes.c_int64, ctypes.c_int32, P, P, P, P, P, P, P]
+    L.xattn_decode.restype = ctypes.c_int
+    L.xattn_decode.argtypes = [pd, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.xattn_cache_append.restype = ctypes.c_int
+    L.xattn_cache_append.argtypes = [pd, P, P, P, P, P, P, P, P, P, P, P]
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().xattn_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != XATTN_OK:
+        raise XattnError(status, where)
+
+
+def _ptr(t):
+    """Device (or host) address of a tensor / None -> NULL."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_dims(*, R, B, Hq, Hkv, D, max_prefix_len, max_unshared_len, dtype, num_slots,
+              num_prefix_tokens, scale, prefix_splits=0, unshared_splits=0) -> Dims:
+    return Dims(int(R), int(B), int(Hq), int(Hkv), int(D), int(max_prefix_len),
+                int(max_unshared_len), int(dtype), int(num_slots), int(num_prefix_tokens),
+                float(scale), int(prefix_splits), int(unshared_splits))
+
+
+def workspace_size(dims: Dims, which: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().xattn_workspace_size(ctypes.byref(dims), int(which), ctypes.byref(n)),
+           "xattn_workspace_size")
+    return int(n.value)
+
+
+def get_plan(dims: Dims, which: int) -> dict:
+    p = Plan()
+    _check(lib().xattn_get_plan(ctypes.byref(dims), int(which), ctypes.byref(p)), "xattn_get_plan")
+    return p.as_dict()
+
+
+def shared_stage(dims, q, k_shared, v_shared, prefix_off, prefix_len, o, lse, workspace=None,
+                 workspace_bytes=0, stream=None):
+    _check(lib().xattn_shared_stage(ctypes.byref(dims), _ptr(q), _ptr(k_shared), _ptr(v_shared),
+                                    _ptr(prefix_off), _ptr(prefix_len), _ptr(o), _ptr(lse),
+                                    _ptr(workspace), int(workspace_bytes), _stream(stream)),
+           "xattn_shared_stage")
+
+
+def unshared_stage(dims, q, k_pool, v_pool, slot_table, unshared_len, o, lse, workspace=None,
+                   workspace_bytes=0, stream=None):
+    _check(lib().xattn_unshared_stage(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                      _ptr(slot_table), _ptr(unshared_len), _ptr(o), _ptr(lse),
+                                      _ptr(workspace), int(workspace_bytes), _stream(stream)),
+           "xattn_unshared_stage")
+
+
+def merge(rows, head_dim, o_a, lse_a, o_b, lse_b, o_out, lse_out=None, stream=None):
+    _check(lib().xattn_merge(int(rows), int(head_dim), _ptr(o_a), _ptr(lse_a), _ptr(o_b),
+                             _ptr(lse_b), _ptr(o_out), _ptr(lse_out), _stream(stream)),
+           "xattn_merge")
+
+
+def decode(dims, q, k_shared, v_shared, prefix_off, prefix_len, k_pool, v_pool, slot_table,
+           unshared_len, o, lse=None, workspace=None, workspace_bytes=0, stream=None):
+    _check(lib().xattn_decode(ctypes.byref(dims), _ptr(q), _ptr(k_shared), _ptr(v_shared),
+                              _ptr(prefix_off), _ptr(prefix_len), _ptr(k_pool), _ptr(v_pool),
+                              _ptr(slot_table), _ptr(unshared_len), _ptr(o), _ptr(lse),
+                              _ptr(workspace), int(workspace_bytes), _stream(stream)),
+           "xattn_decode")
+
+
+def cache_append(dims, k_new, v_new, parent, slot_base, active, k_pool, v_pool, table_in,
+                 table_out, unshared_len, stream=None):
+    _check(lib().xattn_cache_append(ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _ptr(parent),
+                                    _ptr(slot_base), _ptr(active), _ptr(k_pool), _ptr(v_pool),
+                                    _ptr(table_in), _ptr(table_out), _ptr(unshared_len),
+                                    _stream(stream)),
+           "xattn_cache_append")

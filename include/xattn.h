@@ -1,0 +1,195 @@
+/*
+ * xattn.h - staged beam-search decode attention over a split KV cache,
+ * hand-written HIP kernels for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * The method (xGR page, "xGR: Efficient Generative Recommendation Serving at
+ * Scale", section 2.1 xAttention): the KV cache of a generative-recommendation
+ * request is split in two. The Shared cache holds the prompt (user history),
+ * computed once at prefill and read once for all beams of the request. The
+ * Non-Shared cache holds only the tokens generated at each decode step,
+ * managed per token (no blocks), so a beam that branches copies nothing.
+ * Attention is computed in stages: a Shared stage and a Non-Shared stage each
+ * produce local scores and max/sum statistics; a Merge stage combines them
+ * with online softmax. Updates to the Non-Shared cache happen in place through
+ * direct indices with no read-before-write hazard. Section 1 of the same page
+ * states the problem this removes (per-beam reloads of the shared prompt and
+ * block copies on branching).
+ *
+ * CONVENTIONS
+ *  - Every pointer argument named as device memory must point to memory the
+ *    caller allocated on the current HIP device. The library never allocates,
+ *    frees or synchronizes; it only enqueues kernels on `stream` (a
+ *    hipStream_t; NULL = the null stream) and returns.
+ *  - Every condition the host can check is checked before anything is
+ *    launched; on error nothing is enqueued. The contents of device arrays
+ *    (lengths, offsets, slot indices, parents) are trusted: out-of-range
+ *    values are undefined behaviour.
+ *  - Results are deterministic: split counts depend only on the dims, there
+ *    are no atomics, so repeated calls give identical bits.
+ *
+ * NOTATION
+ *  R requests; B beam width; beam n = r*B + b (N_b = R*B beams);
+ *  H_q query heads, H_kv kv heads, G = H_q / H_kv, query head q reads kv head
+ *  q / G; D head dim; P_r prompt (prefix) length of request r; L_r the number
+ *  of generated tokens of request r, counting the current step's own token.
+ *
+ * DEVICE LAYOUTS (row-major, element type per dims.dtype unless stated)
+ *  q            [N_b][H_q][D]
+ *  k_shared     [H_kv][n_ptok][D]   request r owns tokens
+ *  v_shared     [H_kv][n_ptok][D]     [prefix_off[r], prefix_off[r] + P_r);
+ *                                     several requests may alias one range
+ *  prefix_off   [R] int64, prefix_len [R] int32 (0 <= P_r <= max_prefix_len)
+ *  k_pool       [num_slots][H_kv][D]  Non-Shared pool, one slot per token
+ *  v_pool       [num_slots][H_kv][D]
+ *  slot_table   [N_b][max_unshared_len] int32; row n valid on [0, L_r)
+ *  unshared_len [R] int32 (0 <= L_r <= max_unshared_len)
+ *  o            [N_b][H_q][D] float32 (normalized attention output)
+ *  lse          [N_b][H_q] float32, natural-log sum of exp(scale * q.k) over
+ *               the part's keys; -inf (and o = 0) for an empty part.
+ */
+#ifndef XATTN_H
+#define XATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  XATTN_OK = 0,
+  XATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent dims */
+  XATTN_ERR_UNSUPPORTED = 2, /* head_dim / dtype / shape outside the built kernels */
+  XATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than xattn_workspace_size */
+  XATTN_ERR_HIP = 4          /* a HIP launch reported an error */
+} xattn_status;
+
+typedef enum { XATTN_F32 = 0, XATTN_BF16 = 1 } xattn_dtype;
+
+/* Host-side sizes. All arrays are passed separately as device pointers. */
+typedef struct {
+  int32_t num_requests;     /* R >= 0 */
+  int32_t beam_width;       /* B >= 1 */
+  int32_t num_q_heads;      /* H_q >= 1, a multiple of num_kv_heads */
+  int32_t num_kv_heads;     /* H_kv >= 1 */
+  int32_t head_dim;         /* D: 64 or 128 */
+  int32_t max_prefix_len;   /* >= every prefix_len[r]; sizes the prefix split plan */
+  int32_t max_unshared_len; /* T_max >= 1: slot-table row stride, >= every unshared_len[r] */
+  int32_t dtype;            /* xattn_dtype of q and every K/V buffer */
+  int64_t num_slots;        /* capacity of k_pool / v_pool in tokens */
+  int64_t num_prefix_tokens;/* n_ptok: token extent of k_shared / v_shared */
+  float scale;              /* softmax scale applied to q.k (normally 1/sqrt(D)) */
+  int32_t prefix_splits;    /* 0 = automatic; else force this many prefix splits */
+  int32_t unshared_splits;  /* 0 = automatic; else force this many Non-Shared splits
+                               (forces the Non-Shared part out of the fused epilogue) */
+} xattn_dims;
+
+/* Launch plan chosen for a dims (introspection for tests and tuning). */
+typedef struct {
+  int32_t rows_per_block;   /* query rows per Shared-stage workgroup (32 per wave) */
+  int32_t row_tiles;        /* ceil(B*G / rows_per_block) per (request, kv head) */
+  int32_t prefix_splits;    /* key-range splits of the prompt */
+  int32_t prefix_chunk;     /* keys per split (a multiple of 64) */
+  int32_t unshared_splits;  /* 0 = Non-Shared part fused into the Shared epilogue */
+  int32_t unshared_chunk;   /* generated tokens per Non-Shared split */
+  int32_t partials;         /* (O, lse) partial slots in the workspace */
+  int32_t mfma;             /* 1 = bf16 MFMA Shared stage, 0 = fp32 vector path */
+} xattn_plan;
+
+/*
+ * Workspace bytes needed by a call. which: 0 = xattn_shared_stage,
+ * 1 = xattn_unshared_stage, 2 = xattn_decode. A size of 0 means the call needs
+ * no workspace (a null workspace pointer is then allowed).
+ */
+xattn_status xattn_workspace_size(const xattn_dims* dims, int which, size_t* bytes);
+
+/* The plan xattn_decode (which = 2), xattn_shared_stage (0) or
+ * xattn_unshared_stage (1) will use for these dims. */
+xattn_status xattn_get_plan(const xattn_dims* dims, int which, xattn_plan* plan);
+
+/*
+ * Shared stage (xGR page, section 2.1, staged computation): for every request
+ * r and kv head h, all B*G query rows attend to the request's prompt keys
+ * [prefix_off[r], prefix_off[r] + P_r) of k_shared / v_shared. The prompt KV
+ * of a (request, kv head) is streamed from HBM once for all its beams.
+ * Writes o_shared [N_b][H_q][D] and lse_shared [N_b][H_q] (float32, device).
+ * bf16 inputs run on bf16 MFMA with fp32 accumulation; fp32 inputs on the
+ * vector ALUs.
+ */
+xattn_status xattn_shared_stage(const xattn_dims* dims, const void* q, const void* k_shared,
+                                const void* v_shared, const int64_t* prefix_off,
+                                const int32_t* prefix_len, float* o_shared, float* lse_shared,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Non-Shared stage (xGR page, section 2.1, separate KV cache and token-granular
+ * management): every beam n attends to its own generated tokens, the pool
+ * slots slot_table[n][0 .. L_r). Writes o_unshared / lse_unshared (float32).
+ */
+xattn_status xattn_unshared_stage(const xattn_dims* dims, const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* slot_table,
+                                  const int32_t* unshared_len, float* o_unshared,
+                                  float* lse_unshared, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
+ * Merge stage (xGR page, section 2.1: online softmax over the stages' max/sum
+ * statistics): for each of `rows` rows of `head_dim` floats,
+ *   lse = log(exp(lse_a) + exp(lse_b)),
+ *   o   = exp(lse_a - lse) * o_a + exp(lse_b - lse) * o_b,
+ * with an empty part (lse = -inf) contributing nothing and two empty parts
+ * giving o = 0, lse = -inf. All pointers are float32 device memory.
+ * o_out may equal o_a or o_b (in place); lse_out may be NULL or equal
+ * lse_a / lse_b.
+ */
+xattn_status xattn_merge(int64_t rows, int32_t head_dim, const float* o_a, const float* lse_a,
+                         const float* o_b, const float* lse_b, float* o_out, float* lse_out,
+                         void* stream);
+
+/*
+ * Fused decode attention: Shared stage + Non-Shared stage + Merge in one pass
+ * (the measured call). The Non-Shared part runs in the Shared stage's
+ * epilogue when the plan fuses it; otherwise it runs as its own split work
+ * and one reduction merges all partials. Writes o [N_b][H_q][D] and, if lse
+ * is not NULL, lse [N_b][H_q].
+ */
+xattn_status xattn_decode(const xattn_dims* dims, const void* q, const void* k_shared,
+                          const void* v_shared, const int64_t* prefix_off,
+                          const int32_t* prefix_len, const void* k_pool, const void* v_pool,
+                          const int32_t* slot_table, const int32_t* unshared_len, float* o,
+                          float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * In-place token-granular append of one decode step (xGR page, section 2.1,
+ * in-place updates through direct indices without read-before-write
+ * hazards; section 1, block copies on branching are what this avoids).
+ * For every request r with active[r] != 0 (active may be NULL = all), with
+ * t = unshared_len[r] (must be < max_unshared_len) and every new beam b:
+ *   slot                  = slot_base[r] + t*B + b
+ *   k_pool[slot], v_pool[slot] <- k_new[r*B + b], v_new[r*B + b]   ([H_kv][D] each)
+ *   table_out[r*B+b][0..t) <- table_in[r*B + parent[r*B+b]][0..t)  (t > 0 only)
+ *   table_out[r*B+b][t]    <- slot
+ * then unshared_len[r] += 1. Columns beyond t are not written. parent values
+ * are request-local beam indices in [0, B); they are ignored at t = 0.
+ * table_out may equal table_in: every parent row is read before any row is
+ * written, so the in-place result equals the out-of-place one.
+ * k_new / v_new: [N_b][H_kv][D] (dims.dtype); parent [N_b] int32;
+ * slot_base [R] int64; active [R] uint8 or NULL; tables [N_b][T_max] int32;
+ * unshared_len [R] int32 (read, then incremented). Needs no workspace.
+ * Slots must lie in [0, num_slots).
+ */
+xattn_status xattn_cache_append(const xattn_dims* dims, const void* k_new, const void* v_new,
+                                const int32_t* parent, const int64_t* slot_base,
+                                const uint8_t* active, void* k_pool, void* v_pool,
+                                const int32_t* table_in, int32_t* table_out,
+                                int32_t* unshared_len, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* xattn_status_string(xattn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XATTN_H */

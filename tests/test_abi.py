@@ -1,0 +1,122 @@
+"""C-ABI surface and host-side error conventions (CPU only, no kernel runs).
+
+Every call here fails host-side validation, which happens before any HIP
+call, so nothing touches a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from generative_recommendation_beam_amd import xattn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(xattn.LIB_PATH):
+        from generative_recommendation_beam_amd import build
+        build.build()
+    return xattn.lib()
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "xattn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(xattn_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert set(names) == set(xattn.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def dims(**kw):
+    base = dict(R=2, B=4, Hq=8, Hkv=2, D=128, max_prefix_len=100, max_unshared_len=4,
+                dtype=xattn.XATTN_BF16, num_slots=64, num_prefix_tokens=200, scale=0.088)
+    base.update(kw)
+    return xattn.make_dims(**base)
+
+
+FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced here
+
+
+def _decode(d, ws=None, nbytes=0, **over):
+    args = dict(q=FAKE, ks=FAKE, vs=FAKE, poff=FAKE, plen=FAKE, kp=FAKE, vp=FAKE, tab=FAKE,
+                ulen=FAKE, o=FAKE, lse=None)
+    args.update(over)
+    return xattn.lib().xattn_decode(ctypes.byref(d), args["q"], args["ks"], args["vs"],
+                                    args["poff"], args["plen"], args["kp"], args["vp"],
+                                    args["tab"], args["ulen"], args["o"], args["lse"], ws, nbytes,
+                                    None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(D=96), xattn.XATTN_ERR_UNSUPPORTED),
+    (dict(D=256), xattn.XATTN_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), xattn.XATTN_ERR_INVALID_ARG),
+    (dict(B=0), xattn.XATTN_ERR_INVALID_ARG),
+    (dict(R=-1), xattn.XATTN_ERR_INVALID_ARG),
+    (dict(dtype=7), xattn.XATTN_ERR_UNSUPPORTED),
+    (dict(max_unshared_len=0), xattn.XATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), xattn.XATTN_ERR_INVALID_ARG),
+    (dict(B=20000), xattn.XATTN_ERR_UNSUPPORTED),
+])
+def test_invalid_dims_rejected(L, over, code):
+    assert _decode(dims(**over)) == code
+    n = ctypes.c_size_t(0)
+    assert L.xattn_workspace_size(ctypes.byref(dims(**over)), 2, ctypes.byref(n)) == code
+
+
+@pytest.mark.parametrize("name", ["q", "ks", "vs", "poff", "plen", "kp", "vp", "tab", "ulen", "o"])
+def test_null_pointer_rejected(L, name):
+    assert _decode(dims(), **{name: None}) == xattn.XATTN_ERR_INVALID_ARG
+
+
+def test_misaligned_pointer_rejected(L):
+    assert _decode(dims(), q=FAKE + 2) == xattn.XATTN_ERR_INVALID_ARG
+
+
+def test_workspace_too_small_rejected(L):
+    d = dims(prefix_splits=4)
+    need = xattn.workspace_size(d, 2)
+    assert need > 0
+    assert _decode(d) == xattn.XATTN_ERR_WORKSPACE
+    assert _decode(d, ws=FAKE, nbytes=need - 1) == xattn.XATTN_ERR_WORKSPACE
+
+
+def test_plan_introspection(L):
+    d = dims(R=8, B=128, Hq=16, Hkv=4, max_prefix_len=1024, max_unshared_len=3)
+    p = xattn.get_plan(d, 2)
+    assert p["mfma"] == 1 and p["rows_per_block"] in (32, 64, 128)
+    assert p["prefix_chunk"] % 64 == 0 and p["prefix_splits"] * p["prefix_chunk"] >= 1024
+    assert p["unshared_splits"] == 0            # short generated tail is fused
+    d2 = dims(R=4, B=16, Hq=32, Hkv=8, max_prefix_len=4096, max_unshared_len=512)
+    p2 = xattn.get_plan(d2, 2)
+    assert p2["unshared_splits"] > 0 and p2["partials"] == p2["prefix_splits"] + p2["unshared_splits"]
+    p3 = xattn.get_plan(dims(dtype=xattn.XATTN_F32), 2)
+    assert p3["mfma"] == 0
+
+
+def test_merge_argument_checks(L):
+    assert L.xattn_merge(-1, 128, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == xattn.XATTN_ERR_INVALID_ARG
+    assert L.xattn_merge(4, 12, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == xattn.XATTN_ERR_UNSUPPORTED
+    assert L.xattn_merge(4, 128, None, FAKE, FAKE, FAKE, FAKE, None, None) == xattn.XATTN_ERR_INVALID_ARG
+    assert L.xattn_merge(0, 128, None, None, None, None, None, None, None) == xattn.XATTN_OK
+
+
+def test_append_argument_checks(L):
+    d = dims()
+    f = L.xattn_cache_append
+    assert f(ctypes.byref(d), None, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == xattn.XATTN_ERR_INVALID_ARG
+    d2 = dims(num_slots=3)   # fewer slots than beams
+    assert f(ctypes.byref(d2), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == xattn.XATTN_ERR_INVALID_ARG
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert xattn.status_string(s).startswith("XATTN_")

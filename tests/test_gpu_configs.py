@@ -1,0 +1,86 @@
+"""The benchmark-shaped workloads at full size, through the C-ABI, in the
+launch configuration bench.py times (automatic plan, in-place appends).
+
+The oracle recomputes a seeded sample of (beam, query head) rows one by one
+from the definition; the tiny fp32 workload is checked in full. Scaled
+workloads are also redrawn unscaled, where the softmax is far from uniform.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from generative_recommendation_beam_amd import device as dv
+from generative_recommendation_beam_amd import inputs, xattn
+from oracle import attention as oa
+from parity import compare
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    xattn.lib()
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def sample_rows(w, k, seed):
+    rng = np.random.default_rng(seed)
+    n = rng.integers(0, w.N_b, size=k)
+    q = rng.integers(0, w.Hq, size=k)
+    rows = list(zip(n.tolist(), q.tolist()))
+    rows += [(0, 0), (w.N_b - 1, w.Hq - 1)]
+    return rows
+
+
+def run_cfg(cfg, unscaled=False, k=48):
+    w = inputs.config(cfg, unscaled=unscaled)
+    print(f"[cfg {cfg} unscaled={unscaled}] R={w.R} B={w.B} P={int(w.prefix_len.max())} "
+          f"L={w.unshared_len.tolist()[:4]} Hq={w.Hq} Hkv={w.Hkv}", flush=True)
+    d = dv.upload(w)
+    dv.build_cache(d)
+    o, lse, ws, nb = dv.alloc_outputs(d, 2)
+    dv.decode(d, o, lse, ws, nb)
+    torch.cuda.synchronize()
+    o = _np(o)[:d.rows].reshape(w.N_b, w.Hq, w.D)
+    lse = _np(lse)[:d.rows].reshape(w.N_b, w.Hq)
+    rows = sample_rows(w, k, 400)
+    O, L = oa.attention_rows(w, rows)
+    og = np.stack([o[n, q] for n, q in rows])
+    lg = np.array([lse[n, q] for n, q in rows])
+    stats = compare(og, O, lg, L, w.dtype, f"config {cfg} unscaled={unscaled}")
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    return w, o, lse, stats
+
+
+def test_config1_full():
+    w = inputs.config(1)
+    d = dv.upload(w)
+    dv.build_cache(d)
+    o, lse, ws, nb = dv.alloc_outputs(d, 2)
+    dv.decode(d, o, lse, ws, nb)
+    torch.cuda.synchronize()
+    O, L = oa.attention(w)
+    compare(_np(o)[:d.rows].reshape(O.shape), O, _np(lse)[:d.rows].reshape(L.shape), L, "f32",
+            "config 1")
+
+
+@pytest.mark.parametrize("cfg", [2, 3, "4A", "4B", 5])
+def test_config_sampled(cfg):
+    run_cfg(cfg)
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_config_unscaled_sampled(cfg):
+    run_cfg(cfg, unscaled=True)
+
+
+def test_config4_homogeneous_equals_heterogeneous():
+    _, oa_, la, _ = run_cfg("4A", k=8)
+    _, ob_, lb, _ = run_cfg("4B", k=8)
+    compare(oa_, ob_, la, lb, "bf16", "4A vs 4B")

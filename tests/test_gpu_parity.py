@@ -1,0 +1,231 @@
+"""HIP path vs the fp64 oracle, through the C-ABI (needs an MI355X).
+
+Inputs are seeded; the oracle consumes the same values the device is given.
+Sizes here let the oracle finish in seconds while spanning several key tiles,
+several row tiles and ragged tails; the full benchmark-shaped workloads are
+checked on sampled rows in test_gpu_configs.py.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from generative_recommendation_beam_amd import device as dv
+from generative_recommendation_beam_amd import xattn
+from generative_recommendation_beam_amd.inputs import make_workload
+from oracle import attention as oa
+from oracle import append as oapp
+from parity import compare
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    xattn.lib()
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def run_decode(w, **kw):
+    d = dv.upload(w, **kw)
+    dv.build_cache(d)
+    o, lse, ws, nb = dv.alloc_outputs(d, 2)
+    dv.decode(d, o, lse, ws, nb)
+    torch.cuda.synchronize()
+    return d, _np(o)[:d.rows].reshape(w.N_b, w.Hq, w.D), _np(lse)[:d.rows].reshape(w.N_b, w.Hq)
+
+
+CASES = {
+    # name: make_workload kwargs
+    "ragged_small_bf16": dict(R=3, B=5, Hq=8, Hkv=2, D=128, prefix_len=[150, 0, 67], unshared_len=[3, 1, 2], T_max=4),
+    "mfma_multi_tile": dict(R=2, B=40, Hq=8, Hkv=2, D=128, prefix_len=[700, 333], unshared_len=[4, 2]),
+    "d64_bf16": dict(R=2, B=24, Hq=4, Hkv=1, D=64, prefix_len=[257, 130], unshared_len=[2, 3]),
+    "g8_bf16": dict(R=2, B=16, Hq=16, Hkv=2, D=128, prefix_len=[520, 64], unshared_len=[5, 1]),
+    "g1_bf16": dict(R=2, B=20, Hq=2, Hkv=2, D=128, prefix_len=[99, 200], unshared_len=[1, 3]),
+    "g6_bf16": dict(R=1, B=9, Hq=12, Hkv=2, D=128, prefix_len=[131], unshared_len=[2]),
+    "b1_decode_bf16": dict(R=5, B=1, Hq=8, Hkv=2, D=128, prefix_len=[300, 64, 1, 0, 500], unshared_len=[3, 0, 2, 4, 1], T_max=5),
+    "no_prefix_bf16": dict(R=2, B=8, Hq=8, Hkv=2, D=128, prefix_len=[0, 0], unshared_len=[3, 2]),
+    "no_gen_bf16": dict(R=2, B=8, Hq=8, Hkv=2, D=128, prefix_len=[200, 90], unshared_len=[0, 0], T_max=2),
+    "long_gen_bf16": dict(R=2, B=4, Hq=8, Hkv=2, D=128, prefix_len=[300, 100], unshared_len=[70, 45]),
+    "f32_small": dict(R=2, B=4, Hq=4, Hkv=1, D=64, prefix_len=[256, 100], unshared_len=[2, 3], dtype="f32"),
+    "f32_d128": dict(R=1, B=3, Hq=8, Hkv=2, D=128, prefix_len=[190], unshared_len=[2], dtype="f32"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+@pytest.mark.parametrize("std", [1.0, 0.3])
+def test_decode_matches_oracle(name, std):
+    kw = dict(CASES[name])
+    w = make_workload(name, seed_key=(300, zlib.crc32(name.encode()) % 1000, int(std * 10)), qkv_std=std,
+                      parent_dist="uniform", **kw)
+    d, o, lse = run_decode(w)
+    O, L = oa.attention(w)
+    compare(o, O, lse, L, w.dtype, f"decode {name} std={std}")
+
+
+@pytest.mark.parametrize("splits", [(1, 0), (2, 0), (3, 0), (5, 0), (1, 1), (2, 3), (4, 2)])
+def test_decode_forced_splits(splits):
+    ps, us = splits
+    w = make_workload("splits", R=2, B=12, Hq=8, Hkv=2, D=128, prefix_len=[640, 200],
+                      unshared_len=[6, 3], seed_key=(301, ps, us), parent_dist="zipf")
+    d, o, lse = run_decode(w, prefix_splits=ps, unshared_splits=us)
+    plan = xattn.get_plan(d.dims, 2)
+    assert plan["prefix_splits"] >= 1
+    O, L = oa.attention(w)
+    compare(o, O, lse, L, "bf16", f"decode splits={splits} plan={plan}")
+
+
+@pytest.mark.parametrize("name", ["ragged_small_bf16", "mfma_multi_tile", "b1_decode_bf16", "f32_small"])
+@pytest.mark.parametrize("ps", [0, 3])
+def test_shared_stage_matches_oracle(name, ps):
+    w = make_workload(name, seed_key=(302, ps), **CASES[name])
+    d = dv.upload(w, prefix_splits=ps)
+    o, lse, ws, nb = dv.alloc_outputs(d, 0)
+    dv.shared_stage(d, o, lse, ws, nb)
+    torch.cuda.synchronize()
+    O, L = oa.attention(w, include_generated=False)
+    compare(_np(o)[:d.rows].reshape(O.shape), O, _np(lse)[:d.rows].reshape(L.shape), L, w.dtype,
+            f"shared {name}")
+
+
+@pytest.mark.parametrize("name", ["ragged_small_bf16", "long_gen_bf16", "b1_decode_bf16", "f32_small"])
+@pytest.mark.parametrize("us", [0, 4])
+def test_unshared_stage_matches_oracle(name, us):
+    w = make_workload(name, seed_key=(303, us), **CASES[name])
+    d = dv.upload(w, unshared_splits=us)
+    dv.build_cache(d)
+    o, lse, ws, nb = dv.alloc_outputs(d, 1)
+    dv.unshared_stage(d, o, lse, ws, nb)
+    torch.cuda.synchronize()
+    O, L = oa.attention(w, include_prefix=False)
+    compare(_np(o)[:d.rows].reshape(O.shape), O, _np(lse)[:d.rows].reshape(L.shape), L, w.dtype,
+            f"unshared {name}")
+
+
+def test_merge_matches_oracle():
+    rng = np.random.default_rng(7)
+    rows, D = 1000, 128
+    oa_ = rng.standard_normal((rows, D)).astype(np.float32)
+    ob_ = rng.standard_normal((rows, D)).astype(np.float32)
+    la = (rng.standard_normal(rows) * 5).astype(np.float32)
+    lb = (rng.standard_normal(rows) * 5).astype(np.float32)
+    la[::7] = -np.inf
+    lb[::11] = -np.inf
+    t = lambda a: torch.from_numpy(a).cuda()
+    A, Bt, LA, LB = t(oa_), t(ob_), t(la), t(lb)
+    out = torch.empty_like(A)
+    lout = torch.empty_like(LA)
+    xattn.merge(rows, D, A, LA, Bt, LB, out, lout)
+    torch.cuda.synchronize()
+    Om, Lm = oa.merge(oa_, la, ob_, lb)
+    compare(_np(out), Om, _np(lout), Lm, "f32", "merge")
+    # in place: o_out aliases o_a and lse_out aliases lse_a
+    xattn.merge(rows, D, A, LA, Bt, LB, A, LA)
+    torch.cuda.synchronize()
+    compare(_np(A), Om, _np(LA), Lm, "f32", "merge in place")
+
+
+def test_merge_of_stages_equals_decode():
+    w = make_workload("stages", R=2, B=16, Hq=8, Hkv=2, D=128, prefix_len=[500, 77],
+                      unshared_len=[3, 2], seed_key=(304, 0))
+    d = dv.upload(w)
+    dv.build_cache(d)
+    os_, ls_, ws0, n0 = dv.alloc_outputs(d, 0)
+    ou_, lu_, ws1, n1 = dv.alloc_outputs(d, 1)
+    dv.shared_stage(d, os_, ls_, ws0, n0)
+    dv.unshared_stage(d, ou_, lu_, ws1, n1)
+    xattn.merge(d.rows, w.D, os_, ls_, ou_, lu_, os_, ls_)
+    torch.cuda.synchronize()
+    O, L = oa.attention(w)
+    compare(_np(os_)[:d.rows].reshape(O.shape), O, _np(ls_)[:d.rows].reshape(L.shape), L, "bf16",
+            "shared+unshared+merge")
+
+
+# ---------------------------------------------------------------- append
+
+def _oracle_append(w, inplace=True):
+    kpool = np.zeros((w.num_slots, w.Hkv, w.D), dtype=w.k_new.dtype)
+    vpool = np.zeros_like(kpool)
+    table = np.full((w.N_b, w.T_max), -1, dtype=np.int64)
+    ulen = np.zeros(w.R, dtype=np.int64)
+    for t in range(w.T_steps):
+        tout = table if inplace else table.copy()
+        oapp.cache_append(B=w.B, k_new=w.k_new[t], v_new=w.v_new[t], parent=w.parents[t],
+                          slot_base=w.slot_base, active=w.active(t), k_pool=kpool, v_pool=vpool,
+                          table_in=table, table_out=tout, unshared_len=ulen)
+        table = tout
+    return kpool, vpool, table, ulen
+
+
+@pytest.mark.parametrize("parent", ["uniform", "zipf", "identity", "zero", "reverse"])
+@pytest.mark.parametrize("inplace", [True, False])
+def test_append_bit_exact(parent, inplace):
+    w = make_workload("app", R=3, B=37, Hq=4, Hkv=2, D=64, prefix_len=1,
+                      unshared_len=[6, 3, 0], seed_key=(305, 0),
+                      parent_dist="uniform" if parent in ("zero", "reverse") else parent, T_max=7)
+    if parent in ("zero", "reverse"):
+        for t in range(1, w.T_steps):
+            for r in range(w.R):
+                bb = np.arange(w.B)
+                w.parents[t, r * w.B:(r + 1) * w.B] = 0 * bb if parent == "zero" else bb[::-1]
+    d = dv.upload(w)
+    cur = d.table
+    for t in range(w.T_steps):
+        if inplace:
+            dv.append_step(d, t)
+        else:
+            nxt = cur.clone()          # ping-pong: the new table starts as a copy
+            dv.append_step(d, t, table_in=cur, table_out=nxt)
+            cur = nxt
+    torch.cuda.synchronize()
+    kpool, vpool, table, ulen = _oracle_append(w, inplace)
+    assert np.array_equal(_np(d.unshared_len)[:w.R], ulen)
+    assert np.array_equal(_np(cur if not inplace else d.table).astype(np.int64), table)
+    kp = _np(d.k_pool.view(torch.int16)).view(np.uint16) if w.dtype == "bf16" else _np(d.k_pool)
+    vp = _np(d.v_pool.view(torch.int16)).view(np.uint16) if w.dtype == "bf16" else _np(d.v_pool)
+    assert np.array_equal(kp, kpool) and np.array_equal(vp, vpool)
+
+
+def test_append_large_beam_column_chunks():
+    """B large enough that one request's table needs several column chunks."""
+    w = make_workload("appB", R=2, B=3000, Hq=1, Hkv=1, D=64, prefix_len=1, unshared_len=[5, 4],
+                      seed_key=(306, 0), parent_dist="zipf", T_max=5)
+    d = dv.upload(w)
+    dv.build_cache(d)
+    torch.cuda.synchronize()
+    kpool, vpool, table, ulen = _oracle_append(w)
+    assert np.array_equal(_np(d.table).astype(np.int64), table)
+    assert np.array_equal(_np(d.unshared_len)[:w.R], ulen)
+
+
+def test_decode_identical_histories_bitwise():
+    w = make_workload("ih", R=1, B=32, Hq=8, Hkv=2, D=128, prefix_len=300, unshared_len=3,
+                      seed_key=(307, 0))
+    n1, n2 = 3, 17
+    w.q[n2] = w.q[n1]
+    for t in range(w.T_steps):
+        w.parents[t, n2] = w.parents[t, n1]
+        w.k_new[t, n2] = w.k_new[t, n1]
+        w.v_new[t, n2] = w.v_new[t, n1]
+    d, o, lse = run_decode(w)
+    assert np.array_equal(o[n1], o[n2]) and np.array_equal(lse[n1], lse[n2])
+
+
+def test_decode_deterministic():
+    w = make_workload("det", R=2, B=64, Hq=8, Hkv=2, D=128, prefix_len=900, unshared_len=3,
+                      seed_key=(308, 0))
+    d = dv.upload(w, prefix_splits=3)
+    dv.build_cache(d)
+    o, lse, ws, nb = dv.alloc_outputs(d, 2)
+    dv.decode(d, o, lse, ws, nb)
+    o1 = o.clone()
+    dv.decode(d, o, lse, ws, nb)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o1)
