@@ -87,6 +87,9 @@ def main():
     ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--prefix-splits", type=int, default=0, help="override the split plan (0 = auto)")
+    ap.add_argument("--rows-per-block", type=int, default=0, help="override rows per workgroup (0 = auto)")
+    ap.add_argument("--stages", type=int, default=0, help="override LDS pipeline stages (0 = auto)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -111,7 +114,8 @@ def main():
     layers_np = [inputs.config(cfg, layer=l) for l in range(n_layers)]
     layers = []
     for w in layers_np:
-        d = dv.upload(w)
+        d = dv.upload(w, prefix_splits=args.prefix_splits, rows_per_block=args.rows_per_block,
+                      pipeline_stages=args.stages)
         dv.build_cache(d)
         o, lse, ws, nb = dv.alloc_outputs(d, 2)
         layers.append((d, o, lse, ws, nb))
@@ -163,7 +167,7 @@ def main():
         achieved = alg["mfma_flops"] / call_s / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=peak_tflops, unit="TFLOP/s",
                     frac=round(achieved / peak_tflops, 4), traffic=None)
-    roof["kernel"] = "xattn_decode call (%d kernel launches)" % (1 + (plan["partials"] > 0) + (plan["unshared_splits"] > 0))
+    roof["kernel"] = "xattn_decode call (%d kernel launch%s)" % (plan["launches"], "" if plan["launches"] == 1 else "es")
     roof["avg_call_us"] = round(call_us, 3)
     roof["algorithmic_bytes_per_call"] = alg["total"]
     roof["algorithmic_mfma_flops_per_call"] = alg["mfma_flops"]

@@ -6,7 +6,7 @@
 #include <algorithm>
 #include <cstdint>
 
-#include "../../include/xattn.h"
+#include "xattn.h"
 #include "kernels.h"
 
 using namespace xattn;
@@ -19,6 +19,7 @@ constexpr int kMinSplitKeys = 256;     // never split the prompt finer than this
 constexpr int kFuseMaxUnshared = 16;   // T_max up to this: Non-Shared part in the epilogue
 constexpr int kUnsharedChunk = 64;     // generated tokens per Non-Shared split
 constexpr int kMfmaMinRows = 16;       // fewer query rows per (r,h): vector path
+constexpr int kNumCUs = 256;           // MI355X compute units
 
 struct Plan {
   int mfma;
@@ -30,6 +31,7 @@ struct Plan {
   int u_chunk;
   int parts;
   int ngroups;   // vector path: query-head groups per (beam, kv head)
+  int stages;    // MFMA path: LDS pipeline stages (4 if the grid fits the chip at once)
 };
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -51,6 +53,11 @@ xattn_status check_dims(const xattn_dims* d) {
       d->num_prefix_tokens < 0)
     return XATTN_ERR_INVALID_ARG;
   if (d->prefix_splits < 0 || d->unshared_splits < 0) return XATTN_ERR_INVALID_ARG;
+  if (d->rows_per_block != 0 && d->rows_per_block != 32 && d->rows_per_block != 64 &&
+      d->rows_per_block != 128)
+    return XATTN_ERR_INVALID_ARG;
+  if (d->pipeline_stages != 0 && d->pipeline_stages != 2 && d->pipeline_stages != 4)
+    return XATTN_ERR_INVALID_ARG;
   if (!(d->scale == d->scale)) return XATTN_ERR_INVALID_ARG;  // NaN
   if (d->head_dim != 64 && d->head_dim != 128) return XATTN_ERR_UNSUPPORTED;
   if (d->dtype != XATTN_F32 && d->dtype != XATTN_BF16) return XATTN_ERR_UNSUPPORTED;
@@ -81,7 +88,7 @@ Plan make_plan(const xattn_dims* d, int which) {
   if (want_prefix) {
     int64_t base_waves;
     if (p.mfma) {
-      p.waves = M >= 128 ? 4 : (M > 32 ? 2 : 1);
+      p.waves = d->rows_per_block ? d->rows_per_block / 32 : (M >= 128 ? 4 : (M > 32 ? 2 : 1));
       p.row_tiles = (int)cdiv(M, 32 * p.waves);
       base_waves = (int64_t)d->num_requests * d->num_kv_heads * p.row_tiles * p.waves;
     } else {
@@ -124,15 +131,60 @@ Plan make_plan(const xattn_dims* d, int which) {
   if (which == 0) p.parts = p.p_splits > 1 ? p.p_splits : 0;
   else if (which == 1) p.parts = p.u_splits > 1 ? p.u_splits : 0;
   else p.parts = (p.p_splits > 1 || p.u_splits > 0) ? p.p_splits + p.u_splits : 0;
+  // A prompt split merged in-kernel with the Non-Shared tokens as its own
+  // group member needs one more partial slot.
+  if (which == 2 && p.mfma && p.p_splits > 1 && p.u_splits == 0) p.parts = p.p_splits + 1;
+  // Deep LDS pipeline when every workgroup is resident at once anyway.
+  if (p.mfma) {
+    const int64_t members = p.p_splits + ((which == 2 && p.p_splits > 1 && p.u_splits == 0) ? 1 : 0);
+    const int64_t blocks = (int64_t)d->num_requests * d->num_kv_heads * p.row_tiles * members;
+    p.stages = d->pipeline_stages ? d->pipeline_stages : (blocks <= kNumCUs ? 4 : 2);
+  } else {
+    p.stages = 0;
+  }
   return p;
 }
 
-size_t ws_bytes_for(const xattn_dims* d, const Plan& p) {
-  if (p.parts == 0) return 0;
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace layout, the same for every call that needs one, so the counter
+// block sits at the same place whatever call last used the buffer:
+//   [counters: R*H_kv*row_tiles uint32, 256-aligned]   zero between calls
+//   [partial O: parts * N_b*H_q * D float]
+//   [partial lse: parts * N_b*H_q float]
+struct Layout {
+  size_t counters, o, lse, total;
+};
+
+// Does this plan merge prompt splits inside the MFMA kernel?
+// (Partials are addressed with 32-bit byte offsets per split.)
+bool uses_fixup(const xattn_dims* d, const Plan& p, int which) {
   const int64_t rows = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
-  const size_t o = (size_t)p.parts * rows * d->head_dim * sizeof(float);
-  const size_t l = (size_t)p.parts * rows * sizeof(float);
-  return ((o + 255) / 256) * 256 + ((l + 255) / 256) * 256;
+  return p.mfma && p.p_splits > 1 && (which == 0 || (which == 2 && p.u_splits == 0)) &&
+         rows * d->head_dim * 4 < (int64_t)INT32_MAX;
+}
+
+// Kernel launches one call makes under plan p.
+int launches(const xattn_dims* d, const Plan& p, int which) {
+  if (p.parts == 0 || uses_fixup(d, p, which)) return 1;
+  return 2 + ((which == 2 && p.u_splits > 0) ? 1 : 0);
+}
+
+Layout layout_for(const xattn_dims* d, const Plan& p, int which) {
+  Layout L{0, 0, 0, 0};
+  const int64_t rows = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
+  const int parts = p.parts;
+  if (parts == 0) return L;
+  const size_t nctr = (size_t)d->num_requests * d->num_kv_heads * std::max(p.row_tiles, 1);
+  L.counters = 0;
+  L.o = align256(nctr * sizeof(unsigned));
+  L.lse = L.o + align256((size_t)parts * rows * d->head_dim * sizeof(float));
+  L.total = L.lse + align256((size_t)parts * rows * sizeof(float));
+  return L;
+}
+
+size_t ws_bytes_for(const xattn_dims* d, const Plan& p, int which) {
+  return layout_for(d, p, which).total;
 }
 
 Shape make_shape(const xattn_dims* d) {
@@ -149,27 +201,28 @@ Shape make_shape(const xattn_dims* d) {
 }
 
 struct Workspace {
+  unsigned* counters;
   float* o;
   float* lse;
 };
 
-Workspace carve(const xattn_dims* d, const Plan& p, void* ws) {
-  const int64_t rows = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
-  const size_t o = (size_t)p.parts * rows * d->head_dim * sizeof(float);
-  Workspace w;
-  w.o = static_cast<float*>(ws);
-  w.lse = reinterpret_cast<float*>(static_cast<char*>(ws) + ((o + 255) / 256) * 256);
-  return w;
+Workspace carve(const xattn_dims* d, const Plan& p, int which, void* ws) {
+  const Layout L = layout_for(d, p, which);
+  char* base = static_cast<char*>(ws);
+  return Workspace{reinterpret_cast<unsigned*>(base + L.counters),
+                   reinterpret_cast<float*>(base + L.o), reinterpret_cast<float*>(base + L.lse)};
 }
 
 inline xattn_status hip_status(hipError_t e) { return e == hipSuccess ? XATTN_OK : XATTN_ERR_HIP; }
 
-// Launch the prompt pass (MFMA or vector) into `out`, with optional fused
-// Non-Shared epilogue pointers.
-hipError_t run_prefix(const xattn_dims* d, const Plan& p, const void* q, const void* ks,
+// Launch the prompt pass (MFMA or vector). `mode` selects how the MFMA kernel
+// writes (final / partial slot part_base+split / in-kernel split merge).
+// kp != null folds the Non-Shared tokens into prompt split 0.
+hipError_t run_prefix(const xattn_dims* d, const Plan& p, int mode, const void* q, const void* ks,
                       const void* vs, const int64_t* poff, const int32_t* plen, const void* kp,
                       const void* vp, const int32_t* table, const int32_t* ulen, OutSpec out,
-                      hipStream_t st) {
+                      const Workspace& w, hipStream_t st) {
+  const int64_t rows = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
   if (p.mfma) {
     SharedMfmaArgs a;
     a.s = make_shape(d);
@@ -183,10 +236,17 @@ hipError_t run_prefix(const xattn_dims* d, const Plan& p, const void* q, const v
     a.slot_table = table;
     a.unshared_len = ulen;
     a.out = out;
+    a.mode = mode;
+    a.part_o = w.o;
+    a.part_lse = w.lse;
+    a.part_stride = rows;
+    a.counters = w.counters;
     a.waves = p.waves;
     a.row_tiles = p.row_tiles;
     a.p_splits = p.p_splits;
     a.p_chunk = p.p_chunk;
+    a.gen_member = (mode == kModeFixup && kp != nullptr) ? 1 : 0;
+    a.stages = p.stages;
     return launch_shared_mfma(a, st);
   }
   ValuArgs a;
@@ -205,7 +265,7 @@ hipError_t run_prefix(const xattn_dims* d, const Plan& p, const void* q, const v
   a.use_gen = kp != nullptr ? 1 : 0;
   a.splits = p.p_splits;
   a.chunk = p.p_chunk;
-  a.out = out;
+  a.out = mode == kModeFinal ? out : OutSpec{w.o, w.lse, rows, out.part_base};
   return launch_valu_attn(a, st);
 }
 
@@ -260,6 +320,8 @@ xattn_status xattn_get_plan(const xattn_dims* d, int which, xattn_plan* out) {
   out->unshared_chunk = which == 0 ? 0 : p.u_chunk;
   out->partials = p.parts;
   out->mfma = p.mfma;
+  out->launches = launches(d, p, which);
+  out->pipeline_stages = p.stages;
   return XATTN_OK;
 }
 
@@ -267,7 +329,7 @@ xattn_status xattn_workspace_size(const xattn_dims* d, int which, size_t* bytes)
   xattn_status e = check_dims(d);
   if (e != XATTN_OK) return e;
   if (!bytes || which < 0 || which > 2) return XATTN_ERR_INVALID_ARG;
-  *bytes = ws_bytes_for(d, make_plan(d, which));
+  *bytes = ws_bytes_for(d, make_plan(d, which), which);
   return XATTN_OK;
 }
 
@@ -280,17 +342,20 @@ xattn_status xattn_shared_stage(const xattn_dims* d, const void* q, const void* 
   if (!aligned16(q) || !aligned16(o) || !kv_ok(ks, vs, d->num_prefix_tokens))
     return XATTN_ERR_INVALID_ARG;
   const Plan p = make_plan(d, 0);
-  const size_t need = ws_bytes_for(d, p);
+  const size_t need = ws_bytes_for(d, p, 0);
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return XATTN_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t rows = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
-  if (p.parts == 0) {
-    return hip_status(run_prefix(d, p, q, ks, vs, poff, plen, nullptr, nullptr, nullptr, nullptr,
-                                 OutSpec{o, lse, 0, 0}, st));
-  }
-  Workspace w = carve(d, p, ws);
-  hipError_t he = run_prefix(d, p, q, ks, vs, poff, plen, nullptr, nullptr, nullptr, nullptr,
-                             OutSpec{w.o, w.lse, rows, 0}, st);
+  const Workspace w = need > 0 ? carve(d, p, 0, ws) : Workspace{nullptr, nullptr, nullptr};
+  const OutSpec fin{o, lse, 0, 0};
+  if (p.parts == 0)
+    return hip_status(run_prefix(d, p, kModeFinal, q, ks, vs, poff, plen, nullptr, nullptr, nullptr,
+                                 nullptr, fin, w, st));
+  if (uses_fixup(d, p, 0))
+    return hip_status(run_prefix(d, p, kModeFixup, q, ks, vs, poff, plen, nullptr, nullptr, nullptr,
+                                 nullptr, fin, w, st));
+  hipError_t he = run_prefix(d, p, kModePartial, q, ks, vs, poff, plen, nullptr, nullptr, nullptr,
+                             nullptr, fin, w, st);
   if (he != hipSuccess) return XATTN_ERR_HIP;
   return hip_status(launch_merge_parts(rows, d->head_dim, p.parts, w.o, w.lse, o, lse, st));
 }
@@ -303,7 +368,7 @@ xattn_status xattn_unshared_stage(const xattn_dims* d, const void* q, const void
   if (!q || !table || !ulen || !o || !lse) return XATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(o) || !kv_ok(kp, vp, d->num_slots)) return XATTN_ERR_INVALID_ARG;
   const Plan p = make_plan(d, 1);
-  const size_t need = ws_bytes_for(d, p);
+  const size_t need = ws_bytes_for(d, p, 1);
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return XATTN_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t rows = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
@@ -312,7 +377,7 @@ xattn_status xattn_unshared_stage(const xattn_dims* d, const void* q, const void
     p1.u_splits = 1;
     return hip_status(run_gen(d, p1, q, kp, vp, table, ulen, OutSpec{o, lse, 0, 0}, st));
   }
-  Workspace w = carve(d, p, ws);
+  const Workspace w = carve(d, p, 1, ws);
   hipError_t he = run_gen(d, p, q, kp, vp, table, ulen, OutSpec{w.o, w.lse, rows, 0}, st);
   if (he != hipSuccess) return XATTN_ERR_HIP;
   return hip_status(launch_merge_parts(rows, d->head_dim, p.parts, w.o, w.lse, o, lse, st));
@@ -342,19 +407,21 @@ xattn_status xattn_decode(const xattn_dims* d, const void* q, const void* ks, co
       !kv_ok(kp, vp, d->num_slots))
     return XATTN_ERR_INVALID_ARG;
   const Plan p = make_plan(d, 2);
-  const size_t need = ws_bytes_for(d, p);
+  const size_t need = ws_bytes_for(d, p, 2);
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return XATTN_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t rows = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
+  const Workspace w = need > 0 ? carve(d, p, 2, ws) : Workspace{nullptr, nullptr, nullptr};
+  const OutSpec fin{o, lse, 0, 0};
+  if (p.parts == 0)  // one launch: prompt pass with the Non-Shared tokens folded in
+    return hip_status(run_prefix(d, p, kModeFinal, q, ks, vs, poff, plen, kp, vp, table, ulen,
+                                 fin, w, st));
+  if (uses_fixup(d, p, 2))  // one launch: prompt splits merged by their last workgroup
+    return hip_status(run_prefix(d, p, kModeFixup, q, ks, vs, poff, plen, kp, vp, table, ulen,
+                                 fin, w, st));
   const bool fused = p.u_splits == 0;
-  if (p.parts == 0) {
-    // one launch: prompt pass with the Non-Shared tokens folded into its epilogue
-    return hip_status(run_prefix(d, p, q, ks, vs, poff, plen, kp, vp, table, ulen,
-                                 OutSpec{o, lse, 0, 0}, st));
-  }
-  Workspace w = carve(d, p, ws);
-  hipError_t he = run_prefix(d, p, q, ks, vs, poff, plen, fused ? kp : nullptr,
-                             fused ? vp : nullptr, table, ulen, OutSpec{w.o, w.lse, rows, 0}, st);
+  hipError_t he = run_prefix(d, p, kModePartial, q, ks, vs, poff, plen, fused ? kp : nullptr,
+                             fused ? vp : nullptr, table, ulen, fin, w, st);
   if (he != hipSuccess) return XATTN_ERR_HIP;
   if (!fused) {
     he = run_gen(d, p, q, kp, vp, table, ulen, OutSpec{w.o, w.lse, rows, p.p_splits}, st);

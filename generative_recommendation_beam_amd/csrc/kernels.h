@@ -22,6 +22,13 @@ struct Shape {
 };
 
 // ---- Shared stage, bf16 MFMA (shared_mfma.hip) ----
+// kModeFinal: one prompt split, write o/lse. kModePartial: write partial slot
+// out.part_base + split. kModeFixup: write partial slot `split`, and the last
+// workgroup of each (request, kv head, row tile) merges all splits into o/lse.
+constexpr int kModeFinal = 0;
+constexpr int kModePartial = 1;
+constexpr int kModeFixup = 2;
+
 struct SharedMfmaArgs {
   Shape s;
   const uint16_t* q;
@@ -34,11 +41,18 @@ struct SharedMfmaArgs {
   const uint16_t* v_pool;
   const int32_t* slot_table;
   const int32_t* unshared_len;
-  OutSpec out;
+  OutSpec out;      // final outputs (part_base used in kModePartial)
+  int mode;
+  float* part_o;    // [parts][N_b*H_q][D] partial outputs (modes partial / fixup)
+  float* part_lse;  // [parts][N_b*H_q]
+  int64_t part_stride;  // N_b*H_q
+  unsigned* counters;   // [R*H_kv*row_tiles], zero between calls (fixup)
   int waves;        // waves per block: 1, 2 or 4 (32 query rows each)
   int row_tiles;
   int p_splits;
   int p_chunk;      // multiple of 64
+  int gen_member;   // kModeFixup with k_pool: one extra member per group does the Non-Shared tokens
+  int stages;       // LDS pipeline stages: 2 or 4
 };
 hipError_t launch_shared_mfma(const SharedMfmaArgs& a, hipStream_t st);
 

@@ -48,13 +48,14 @@ class DeviceWorkload:
 
 
 def upload(w: Workload, device="cuda", *, prefix_splits=0, unshared_splits=0,
-           table_fill: int = -1) -> DeviceWorkload:
+           rows_per_block=0, pipeline_stages=0, table_fill: int = -1) -> DeviceWorkload:
     dims = xattn.make_dims(R=w.R, B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
                            max_prefix_len=int(w.prefix_len.max()) if w.R else 0,
                            max_unshared_len=w.T_max,
                            dtype=xattn.XATTN_BF16 if w.dtype == "bf16" else xattn.XATTN_F32,
                            num_slots=w.num_slots, num_prefix_tokens=w.n_ptok, scale=w.scale,
-                           prefix_splits=prefix_splits, unshared_splits=unshared_splits)
+                           prefix_splits=prefix_splits, unshared_splits=unshared_splits,
+                           rows_per_block=rows_per_block, pipeline_stages=pipeline_stages)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     T = w.T_steps
     act = np.stack([w.active(t) for t in range(T)]) if T else np.zeros((0, w.R), np.uint8)
@@ -92,7 +93,7 @@ def alloc_outputs(d: DeviceWorkload, which: int = 2):
     o = torch.empty((max(d.rows, 1), d.w.D), dtype=torch.float32, device=dev)
     lse = torch.empty(max(d.rows, 1), dtype=torch.float32, device=dev)
     nbytes = xattn.workspace_size(d.dims, which)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)  # counters start at zero
     return o, lse, ws, nbytes
 
 

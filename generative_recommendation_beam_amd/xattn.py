@@ -30,14 +30,16 @@ class Dims(ctypes.Structure):
                 ("max_unshared_len", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("num_slots", ctypes.c_int64), ("num_prefix_tokens", ctypes.c_int64),
                 ("scale", ctypes.c_float), ("prefix_splits", ctypes.c_int32),
-                ("unshared_splits", ctypes.c_int32)]
+                ("unshared_splits", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
+                ("pipeline_stages", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
     _fields_ = [("rows_per_block", ctypes.c_int32), ("row_tiles", ctypes.c_int32),
                 ("prefix_splits", ctypes.c_int32), ("prefix_chunk", ctypes.c_int32),
                 ("unshared_splits", ctypes.c_int32), ("unshared_chunk", ctypes.c_int32),
-                ("partials", ctypes.c_int32), ("mfma", ctypes.c_int32)]
+                ("partials", ctypes.c_int32), ("mfma", ctypes.c_int32),
+                ("launches", ctypes.c_int32), ("pipeline_stages", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -61,7 +63,7 @@ def lib():
         raise RuntimeError(f"xattn HIP library not built: {LIB_PATH} is missing "
                            "(run __graft_entry__.build() or python -m "
                            "generative_recommendation_beam_amd.build)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
     P = ctypes.c_void_p
     pd = ctypes.POINTER(Dims)
     L.xattn_status_string.restype = ctypes.c_char_p
@@ -110,10 +112,12 @@ def _stream(stream):
 
 
 def make_dims(*, R, B, Hq, Hkv, D, max_prefix_len, max_unshared_len, dtype, num_slots,
-              num_prefix_tokens, scale, prefix_splits=0, unshared_splits=0) -> Dims:
+              num_prefix_tokens, scale, prefix_splits=0, unshared_splits=0, rows_per_block=0,
+              pipeline_stages=0) -> Dims:
     return Dims(int(R), int(B), int(Hq), int(Hkv), int(D), int(max_prefix_len),
                 int(max_unshared_len), int(dtype), int(num_slots), int(num_prefix_tokens),
-                float(scale), int(prefix_splits), int(unshared_splits))
+                float(scale), int(prefix_splits), int(unshared_splits), int(rows_per_block),
+                int(pipeline_stages))
 
 
 def workspace_size(dims: Dims, which: int) -> int:

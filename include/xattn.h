@@ -24,8 +24,9 @@
  *    launched; on error nothing is enqueued. The contents of device arrays
  *    (lengths, offsets, slot indices, parents) are trusted: out-of-range
  *    values are undefined behaviour.
- *  - Results are deterministic: split counts depend only on the dims, there
- *    are no atomics, so repeated calls give identical bits.
+ *  - Results are deterministic: split counts depend only on the dims and
+ *    partial results are always combined in the same order, so repeated calls
+ *    give identical bits (a counter only decides which workgroup combines).
  *
  * NOTATION
  *  R requests; B beam width; beam n = r*B + b (N_b = R*B beams);
@@ -83,6 +84,9 @@ typedef struct {
   int32_t prefix_splits;    /* 0 = automatic; else force this many prefix splits */
   int32_t unshared_splits;  /* 0 = automatic; else force this many Non-Shared splits
                                (forces the Non-Shared part out of the fused epilogue) */
+  int32_t rows_per_block;   /* 0 = automatic; else 32, 64 or 128 query rows per
+                               Shared-stage workgroup (bf16 MFMA path) */
+  int32_t pipeline_stages;  /* 0 = automatic; else 2 or 4 K/V tiles staged in LDS */
 } xattn_dims;
 
 /* Launch plan chosen for a dims (introspection for tests and tuning). */
@@ -94,13 +98,20 @@ typedef struct {
   int32_t unshared_splits;  /* 0 = Non-Shared part fused into the Shared epilogue */
   int32_t unshared_chunk;   /* generated tokens per Non-Shared split */
   int32_t partials;         /* (O, lse) partial slots in the workspace */
-  int32_t mfma;             /* 1 = bf16 MFMA Shared stage, 0 = fp32 vector path */
+  int32_t mfma;             /* 1 = bf16 MFMA Shared stage, 0 = vector-ALU path */
+  int32_t launches;         /* kernel launches per call */
+  int32_t pipeline_stages;  /* K/V tiles staged in LDS (MFMA path) */
 } xattn_plan;
 
 /*
  * Workspace bytes needed by a call. which: 0 = xattn_shared_stage,
  * 1 = xattn_unshared_stage, 2 = xattn_decode. A size of 0 means the call needs
  * no workspace (a null workspace pointer is then allowed).
+ * The workspace (device memory, 16-byte aligned, owned by the caller) starts
+ * with a block of split counters that must be zero-filled before the buffer's
+ * first use; every call returns them to zero, so a buffer is reusable by any
+ * later call. Calls that may run at the same time (e.g. on different streams)
+ * must not share a workspace.
  */
 xattn_status xattn_workspace_size(const xattn_dims* dims, int which, size_t* bytes);
 

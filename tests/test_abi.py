@@ -120,3 +120,18 @@ def test_append_argument_checks(L):
 def test_status_strings(L):
     for s in range(5):
         assert xattn.status_string(s).startswith("XATTN_")
+
+
+def test_library_has_no_undefined_internal_symbols(L):
+    """Every kernel launch stub the library references is defined in it (a
+    host-pass compile problem once left kernel stubs undefined, which only
+    showed up when the library was loaded with every symbol resolved)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", xattn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    bad = [l for l in out.splitlines() if "xattn" in l]
+    assert not bad, bad

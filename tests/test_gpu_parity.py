@@ -218,6 +218,25 @@ def test_decode_identical_histories_bitwise():
     assert np.array_equal(o[n1], o[n2]) and np.array_equal(lse[n1], lse[n2])
 
 
+def test_workspace_reuse_across_split_counts():
+    """One zero-initialised workspace serves repeated calls with different
+    split counts: the in-kernel split counters return to zero after each."""
+    w = make_workload("reuse", R=2, B=32, Hq=8, Hkv=2, D=128, prefix_len=[900, 700],
+                      unshared_len=[3, 2], seed_key=(309, 0))
+    O, L = oa.attention(w)
+    d = dv.upload(w, prefix_splits=7)
+    dv.build_cache(d)
+    _, _, ws, nb = dv.alloc_outputs(d, 2)
+    for ps in (7, 3, 7, 2, 5, 5):
+        d.dims.prefix_splits = ps
+        o, lse, _, nb2 = dv.alloc_outputs(d, 2)
+        assert nb2 <= ws.numel()
+        dv.decode(d, o, lse, ws, ws.numel())
+        torch.cuda.synchronize()
+        compare(_np(o)[:d.rows].reshape(O.shape), O, _np(lse)[:d.rows].reshape(L.shape), L, "bf16",
+                f"reuse ps={ps}")
+
+
 def test_decode_deterministic():
     w = make_workload("det", R=2, B=64, Hq=8, Hkv=2, D=128, prefix_len=900, unshared_len=3,
                       seed_key=(308, 0))
