@@ -78,6 +78,49 @@ def cpu_baseline(layers_np, min_seconds=10.0):
                        f"(fp64 numpy oracle, {used} worker processes, {el:.1f} s)")
 
 
+KERNEL_SOURCES = ("generative_recommendation_beam_amd/csrc/shared_mfma.hip",
+                  "generative_recommendation_beam_amd/csrc/device.h",
+                  "generative_recommendation_beam_amd/csrc/kernels.h",
+                  "generative_recommendation_beam_amd/csrc/api.cpp")
+
+
+def kernel_hash():
+    """Hash of the sources of the Shared-stage kernel and its launch plan."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cfg):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counts, each scaled by the same counter's reading for a plain copy of known
+    size; None if absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    e = t.get("workloads", {}).get(str(cfg))
+    if not e or e.get("kernel_hash") != kernel_hash():
+        return None
+    cal = t["copy_calibration"]
+    return int(e["fetch_kib"] * 1024 * cal["fetch_factor"] + e["write_kib"] * 1024 * cal["write_factor"])
+
+
+def calibrate_copy(nbytes, reps):
+    """A plain device copy of known size, for scaling byte counters."""
+    import torch
+    torch.cuda.set_device(0)
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,7 +133,12 @@ def main():
     ap.add_argument("--prefix-splits", type=int, default=0, help="override the split plan (0 = auto)")
     ap.add_argument("--rows-per-block", type=int, default=0, help="override rows per workgroup (0 = auto)")
     ap.add_argument("--stages", type=int, default=0, help="override LDS pipeline stages (0 = auto)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, 3)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(requests shard across GPUs with no exchange; see the design notes).",
@@ -162,15 +210,16 @@ def main():
     if t_hbm >= t_mfma:
         achieved = alg["total"] / call_s / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None)
+                    frac=round(achieved / PEAK_HBM_GBS, 4), traffic=measured_traffic(cfg))
     else:
         achieved = alg["mfma_flops"] / call_s / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=peak_tflops, unit="TFLOP/s",
-                    frac=round(achieved / peak_tflops, 4), traffic=None)
+                    frac=round(achieved / peak_tflops, 4), traffic=measured_traffic(cfg))
     roof["kernel"] = "xattn_decode call (%d kernel launch%s)" % (plan["launches"], "" if plan["launches"] == 1 else "es")
     roof["avg_call_us"] = round(call_us, 3)
     roof["algorithmic_bytes_per_call"] = alg["total"]
     roof["algorithmic_mfma_flops_per_call"] = alg["mfma_flops"]
+    roof["kernel_hash"] = kernel_hash()
 
     result = {
         "metric": "beam-decode attention beams*layer-steps/s; achieved HBM GB/s vs peak",

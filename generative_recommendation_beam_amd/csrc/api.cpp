@@ -14,7 +14,11 @@ using namespace xattn;
 namespace {
 
 constexpr int kMaxBeamWidth = 16384;   // one request's table chunk must fit in LDS
-constexpr int kTargetWaves = 2048;     // enough resident waves to cover 256 CUs
+constexpr int kTargetWaves = 2048;     // vector path: resident waves to cover 256 CUs
+// MFMA path: split the prompt only until this many workgroups exist. Measured
+// on MI355X, a split's partial write and in-kernel merge cost more than the
+// extra parallelism returns once half the CUs hold a workgroup.
+constexpr int kTargetMfmaBlocks = 128;
 constexpr int kMinSplitKeys = 256;     // never split the prompt finer than this
 constexpr int kFuseMaxUnshared = 16;   // T_max up to this: Non-Shared part in the epilogue
 constexpr int kUnsharedChunk = 64;     // generated tokens per Non-Shared split
@@ -31,7 +35,7 @@ struct Plan {
   int u_chunk;
   int parts;
   int ngroups;   // vector path: query-head groups per (beam, kv head)
-  int stages;    // MFMA path: LDS pipeline stages (4 if the grid fits the chip at once)
+  int stages;    // MFMA path: LDS pipeline stages
 };
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -86,21 +90,23 @@ Plan make_plan(const xattn_dims* d, int which) {
   p.p_splits = 1;
   p.p_chunk = std::max(64, (int)cdiv(std::max(maxP, 1), 64) * 64);
   if (want_prefix) {
-    int64_t base_waves;
+    int64_t base_units, target_units;
     if (p.mfma) {
       p.waves = d->rows_per_block ? d->rows_per_block / 32 : (M >= 128 ? 4 : (M > 32 ? 2 : 1));
       p.row_tiles = (int)cdiv(M, 32 * p.waves);
-      base_waves = (int64_t)d->num_requests * d->num_kv_heads * p.row_tiles * p.waves;
+      base_units = (int64_t)d->num_requests * d->num_kv_heads * p.row_tiles;  // workgroups
+      target_units = kTargetMfmaBlocks;
     } else {
       p.waves = 1;
       p.row_tiles = 1;
-      base_waves = N_b * d->num_kv_heads * p.ngroups;
+      base_units = N_b * d->num_kv_heads * p.ngroups;  // wavefronts
+      target_units = kTargetWaves;
     }
     int s;
     if (d->prefix_splits > 0) {
       s = d->prefix_splits;
     } else {
-      s = base_waves > 0 ? (int)cdiv(kTargetWaves, base_waves) : 1;
+      s = base_units > 0 ? (int)cdiv(target_units, base_units) : 1;
       s = (int)std::min<int64_t>(s, std::max<int64_t>(1, cdiv(maxP, kMinSplitKeys)));
       s = std::max(s, 1);
     }
@@ -134,14 +140,9 @@ Plan make_plan(const xattn_dims* d, int which) {
   // A prompt split merged in-kernel with the Non-Shared tokens as its own
   // group member needs one more partial slot.
   if (which == 2 && p.mfma && p.p_splits > 1 && p.u_splits == 0) p.parts = p.p_splits + 1;
-  // Deep LDS pipeline when every workgroup is resident at once anyway.
-  if (p.mfma) {
-    const int64_t members = p.p_splits + ((which == 2 && p.p_splits > 1 && p.u_splits == 0) ? 1 : 0);
-    const int64_t blocks = (int64_t)d->num_requests * d->num_kv_heads * p.row_tiles * members;
-    p.stages = d->pipeline_stages ? d->pipeline_stages : (blocks <= kNumCUs ? 4 : 2);
-  } else {
-    p.stages = 0;
-  }
+  // Two LDS stages measured best on every workload (four fit only one
+  // workgroup per CU and push accumulators into AGPRs); four on request.
+  p.stages = p.mfma ? (d->pipeline_stages ? d->pipeline_stages : 2) : 0;
   return p;
 }
 
