@@ -133,6 +133,7 @@ def main():
     ap.add_argument("--prefix-splits", type=int, default=0, help="override the split plan (0 = auto)")
     ap.add_argument("--rows-per-block", type=int, default=0, help="override rows per workgroup (0 = auto)")
     ap.add_argument("--stages", type=int, default=0, help="override LDS pipeline stages (0 = auto)")
+    ap.add_argument("--key-groups", type=int, default=0, help="override key groups per workgroup (0 = auto)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -163,7 +164,7 @@ def main():
     layers = []
     for w in layers_np:
         d = dv.upload(w, prefix_splits=args.prefix_splits, rows_per_block=args.rows_per_block,
-                      pipeline_stages=args.stages)
+                      pipeline_stages=args.stages, key_groups=args.key_groups)
         dv.build_cache(d)
         o, lse, ws, nb = dv.alloc_outputs(d, 2)
         layers.append((d, o, lse, ws, nb))

@@ -23,6 +23,7 @@ constexpr int kMinSplitKeys = 256;     // never split the prompt finer than this
 constexpr int kFuseMaxUnshared = 16;   // T_max up to this: Non-Shared part in the epilogue
 constexpr int kUnsharedChunk = 64;     // generated tokens per Non-Shared split
 constexpr int kMfmaMinRows = 16;       // fewer query rows per (r,h): vector path
+constexpr int kKeyGroupMinKeys = 512;  // automatic key groups only for prompts this long
 constexpr int kNumCUs = 256;           // MI355X compute units
 
 struct Plan {
@@ -36,6 +37,7 @@ struct Plan {
   int parts;
   int ngroups;   // vector path: query-head groups per (beam, kv head)
   int stages;    // MFMA path: LDS pipeline stages
+  int kgroups;   // MFMA path: wave groups taking alternate key tiles of the same rows
 };
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -62,6 +64,8 @@ xattn_status check_dims(const xattn_dims* d) {
     return XATTN_ERR_INVALID_ARG;
   if (d->pipeline_stages != 0 && d->pipeline_stages != 2 && d->pipeline_stages != 4)
     return XATTN_ERR_INVALID_ARG;
+  if (d->key_groups < 0 || d->key_groups > 2) return XATTN_ERR_INVALID_ARG;
+  if (d->key_groups == 2 && d->pipeline_stages == 4) return XATTN_ERR_INVALID_ARG;  // LDS
   if (!(d->scale == d->scale)) return XATTN_ERR_INVALID_ARG;  // NaN
   if (d->head_dim != 64 && d->head_dim != 128) return XATTN_ERR_UNSUPPORTED;
   if (d->dtype != XATTN_F32 && d->dtype != XATTN_BF16) return XATTN_ERR_UNSUPPORTED;
@@ -74,6 +78,7 @@ xattn_status check_dims(const xattn_dims* d) {
 // which: 0 shared stage, 1 unshared stage, 2 decode
 Plan make_plan(const xattn_dims* d, int which) {
   Plan p{};
+  p.kgroups = 1;
   const int G = d->num_q_heads / d->num_kv_heads;
   const int64_t M = (int64_t)d->beam_width * G;
   const int64_t N_b = (int64_t)d->num_requests * d->beam_width;
@@ -92,8 +97,21 @@ Plan make_plan(const xattn_dims* d, int which) {
   if (want_prefix) {
     int64_t base_units, target_units;
     if (p.mfma) {
-      p.waves = d->rows_per_block ? d->rows_per_block / 32 : (M >= 128 ? 4 : (M > 32 ? 2 : 1));
-      p.row_tiles = (int)cdiv(M, 32 * p.waves);
+      int rows = d->rows_per_block ? d->rows_per_block : (M >= 128 ? 128 : (M > 32 ? 64 : 32));
+      int kg = d->key_groups ? d->key_groups : 1;
+      if (d->key_groups == 0 && d->rows_per_block == 0 && d->pipeline_stages != 4 && M >= 64 &&
+          (int64_t)d->num_requests * d->num_kv_heads * cdiv(M, rows) < kNumCUs &&
+          maxP >= kKeyGroupMinKeys) {
+        // Too few (request, kv head, row tile) workgroups to cover the CUs:
+        // halve the rows per workgroup and give each half of its waves
+        // alternate key tiles, so twice the workgroups run with the same
+        // waves each and every wave walks half the prompt.
+        rows = 64;
+        kg = 2;
+      }
+      p.kgroups = kg;
+      p.waves = rows / 32 * kg;
+      p.row_tiles = (int)cdiv(M, rows);
       base_units = (int64_t)d->num_requests * d->num_kv_heads * p.row_tiles;  // workgroups
       target_units = kTargetMfmaBlocks;
     } else {
@@ -248,6 +266,7 @@ hipError_t run_prefix(const xattn_dims* d, const Plan& p, int mode, const void* 
     a.p_chunk = p.p_chunk;
     a.gen_member = (mode == kModeFixup && kp != nullptr) ? 1 : 0;
     a.stages = p.stages;
+    a.key_groups = p.kgroups;
     return launch_shared_mfma(a, st);
   }
   ValuArgs a;
@@ -313,7 +332,7 @@ xattn_status xattn_get_plan(const xattn_dims* d, int which, xattn_plan* out) {
   if (e != XATTN_OK) return e;
   if (!out || which < 0 || which > 2) return XATTN_ERR_INVALID_ARG;
   const Plan p = make_plan(d, which);
-  out->rows_per_block = p.mfma ? 32 * p.waves : 0;
+  out->rows_per_block = p.mfma ? 32 * p.waves / p.kgroups : 0;
   out->row_tiles = p.mfma ? p.row_tiles : 0;
   out->prefix_splits = which == 1 ? 0 : p.p_splits;
   out->prefix_chunk = which == 1 ? 0 : p.p_chunk;
@@ -323,6 +342,7 @@ xattn_status xattn_get_plan(const xattn_dims* d, int which, xattn_plan* out) {
   out->mfma = p.mfma;
   out->launches = launches(d, p, which);
   out->pipeline_stages = p.stages;
+  out->key_groups = p.mfma ? p.kgroups : 0;
   return XATTN_OK;
 }
 

@@ -47,12 +47,13 @@ struct SharedMfmaArgs {
   float* part_lse;  // [parts][N_b*H_q]
   int64_t part_stride;  // N_b*H_q
   unsigned* counters;   // [R*H_kv*row_tiles], zero between calls (fixup)
-  int waves;        // waves per block: 1, 2 or 4 (32 query rows each)
+  int waves;        // waves per block: 1, 2, 4 or 8 (32 query rows each per key group)
   int row_tiles;
   int p_splits;
   int p_chunk;      // multiple of 64
   int gen_member;   // kModeFixup with k_pool: one extra member per group does the Non-Shared tokens
   int stages;       // LDS pipeline stages: 2 or 4
+  int key_groups;   // 1, or 2: waves/2 query rows per block, alternate 64-key tiles per half
 };
 hipError_t launch_shared_mfma(const SharedMfmaArgs& a, hipStream_t st);
 

@@ -73,23 +73,31 @@ __device__ __forceinline__ int swz_k(int key) { return D == 128 ? (key & 15) : (
 template <int D>
 __device__ __forceinline__ int swz_v(int key) { return D == 128 ? ((key & 3) << 2) : ((key & 1) << 2); }
 
-// Per-lane byte offsets (within a tile) of the global chunks this lane loads
-// for each of its direct-load instructions j (instruction index
-// i = wave + NW*j): K then V. Loop-invariant.
-template <int D, int NW>
+// A workgroup loads KG consecutive 64-key tiles per step (a super-tile); its
+// NW waves share the KG*NINST direct-load instructions per tensor. Wave w
+// issues instructions i = w + NW*j; instruction i fills 1 KiB of tile
+// sub = i / NINST at LDS offset (i % NINST) * 1024. Per-lane byte offsets of
+// the global chunks (relative to the super-tile start) for each j, K then V,
+// are loop-invariant.
+template <int D, int NW, int KG>
 struct LoadPlan {
-  static constexpr int NJ = TileGeom<D>::NINST / NW;
+  using TG = TileGeom<D>;
+  static_assert(TG::NINST % NW == 0, "waves must divide the load instructions of a tile");
+  static constexpr int NJ = KG * TG::NINST / NW;
+  // tile index and the wave-independent part of the LDS offset of load j
+  static constexpr int sub(int j) { return NW * j / TG::NINST; }
+  static constexpr int lds_off(int j) { return sub(j) * TG::BUFB + (NW * j - sub(j) * TG::NINST) * 1024; }
   uint32_t k[NJ];
   uint32_t v[NJ];
   __device__ __forceinline__ void init(int wave, int lane) {
-    using TG = TileGeom<D>;
     const int kin = lane / TG::NCH;
     const int pos = lane % TG::NCH;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int key = (wave + NW * j) * TG::KPI + kin;
-      k[j] = (uint32_t)(key * TG::ROWB + (pos ^ swz_k<D>(key)) * 16);
-      v[j] = (uint32_t)(key * TG::ROWB + (pos ^ swz_v<D>(key)) * 16);
+      const int key = (wave + NW * j - sub(j) * TG::NINST) * TG::KPI + kin;  // key within its tile
+      const uint32_t t0 = (uint32_t)(sub(j) * TG::TILEB);  // global byte offset of that tile
+      k[j] = t0 + (uint32_t)(key * TG::ROWB + (pos ^ swz_k<D>(key)) * 16);
+      v[j] = t0 + (uint32_t)(key * TG::ROWB + (pos ^ swz_v<D>(key)) * 16);
     }
   }
 };
@@ -215,74 +223,91 @@ __device__ __forceinline__ void wait_tiles(int ahead) {
 
 constexpr int kMaxFusedTokens = 16;  // Non-Shared tokens folded into the Shared pass
 
-// Online-softmax update with the beam's own generated tokens (the Non-Shared
-// stage): slot indices are fetched first, then each token costs one round
-// trip for its K and V rows. Lane (hh, c) holds head-dim halves of query row
-// c, so the dot product needs one exchange with lane c + 32.
+// The Non-Shared stage folded into a Shared-stage wave: the beam's own
+// generated tokens, gathered through its slot-table row. Lane (hh, c) holds
+// head-dim halves of query row c, so a dot product needs one exchange with
+// lane c + 32. With key groups, group kg takes tokens kg, kg + KG, ...
+template <int D, int KG>
+struct NonShared {
+  static constexpr int NDC = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int NT = kMaxFusedTokens / KG;  // tokens per wave at most
+  int L;  // generated tokens of the request (uniform)
+  int kg;
+  const int32_t* trow;  // the beam's slot-table row
+  const uint16_t* kp;
+  const uint16_t* vp;
+  int hkv;
+
+  __device__ __forceinline__ void init(const SharedMfmaArgs& a, int r, int h, int bq, int kg_, int hh) {
+    const Shape& s = a.s;
+    kg = kg_;
+    L = __builtin_amdgcn_readfirstlane(a.unshared_len[r]);
+    hkv = s.Hkv;
+    kp = a.k_pool + (int64_t)h * D + 8 * hh;
+    vp = a.v_pool + (int64_t)h * D + 4 * hh;
+    trow = a.slot_table + ((int64_t)r * s.B + bq) * s.T_max;
+  }
+  // Does this wave take a u-th token (token kg + KG*u)?
+  __device__ __forceinline__ bool has(int u) const { return kg + KG * u < L; }
+  __device__ __forceinline__ int slot(int u) const { return has(u) ? trow[kg + KG * u] : 0; }
+
+  // This lane's parts of the K and V rows in pool slot `sl`.
+  __device__ __forceinline__ void fetch(int sl, uint4* kk, uint2 (*vv)[4]) const {
+    const int64_t row = (int64_t)sl * hkv * D;
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) kk[dc] = *reinterpret_cast<const uint4*>(kp + row + 16 * dc);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) vv[db][ig] = *reinterpret_cast<const uint2*>(vp + row + 32 * db + 8 * ig);
+  }
+};
+
+// Online-softmax update with one generated token whose K/V parts are in
+// registers.
 template <int D>
-__device__ __forceinline__ void nonshared_update(const SharedMfmaArgs& a, int r, int h, int bq,
-                                                 const bf16x8_t* qf, f32x16_t* oacc, float& m_run,
-                                                 float& l_part, float c, int hh) {
+__device__ __forceinline__ void token_update(const uint4* kk, const uint2 (*vv)[4], const bf16x8_t* qf,
+                                             f32x16_t* oacc, float& m_run, float& l_part, float c, int hh) {
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
-  const Shape& s = a.s;
-  const int L = __builtin_amdgcn_readfirstlane(a.unshared_len[r]);
-  const int32_t* trow = a.slot_table + ((int64_t)r * s.B + bq) * s.T_max;
-  int slots[kMaxFusedTokens];
+  float dot = 0.f;
 #pragma unroll
-  for (int t = 0; t < kMaxFusedTokens; ++t) slots[t] = t < L ? trow[t] : 0;
+  for (int dc = 0; dc < NDC; ++dc) {
+    const bf16x8_t k8 = __builtin_bit_cast(bf16x8_t, kk[dc]);
 #pragma unroll
-  for (int t = 0; t < kMaxFusedTokens; ++t) {
-    if (t >= L) break;
-    const int64_t row = ((int64_t)slots[t] * s.Hkv + h) * D;
-    const uint16_t* kp = a.k_pool + row + 8 * hh;
-    const uint16_t* vp = a.v_pool + row + 4 * hh;
-    uint4 kk[NDC];
-    uint2 vv[NDB][4];
-#pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) kk[dc] = *reinterpret_cast<const uint4*>(kp + 16 * dc);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int ig = 0; ig < 4; ++ig) vv[db][ig] = *reinterpret_cast<const uint2*>(vp + 32 * db + 8 * ig);
-    float dot = 0.f;
-#pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) {
-      const bf16x8_t k8 = __builtin_bit_cast(bf16x8_t, kk[dc]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dot += (float)qf[dc][j] * (float)k8[j];
-    }
-    dot += __shfl_xor(dot, 32);
-    const float st = dot * c;
-    if (st > m_run) {
-      const float alpha = exp2_approx(m_run - st);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      l_part *= alpha;
-      m_run = st;
-    }
-    const float p = exp2_approx(st - m_run);
-    if (hh == 0) l_part += p;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        const uint2 u = vv[db][ig];
-        oacc[db][4 * ig + 0] += p * bf16_bits_to_f32(u.x & 0xffffu);
-        oacc[db][4 * ig + 1] += p * __uint_as_float(u.x & 0xffff0000u);
-        oacc[db][4 * ig + 2] += p * bf16_bits_to_f32(u.y & 0xffffu);
-        oacc[db][4 * ig + 3] += p * __uint_as_float(u.y & 0xffff0000u);
-      }
+    for (int j = 0; j < 8; ++j) dot += (float)qf[dc][j] * (float)k8[j];
   }
-}
-
-template <int D>
-__device__ __forceinline__ void store_rows(float* dst, const f32x16_t* oacc) {
-  constexpr int NDB = D / 32;
+  dot += __shfl_xor(dot, 32);
+  const float st = dot * c;
+  if (st > m_run) {
+    const float alpha = exp2_approx(m_run - st);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    l_part *= alpha;
+    m_run = st;
+  }
+  const float p = exp2_approx(st - m_run);
+  if (hh == 0) l_part += p;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int ig = 0; ig < 4; ++ig) {
+      const uint2 u = vv[db][ig];
+      oacc[db][4 * ig + 0] += p * bf16_bits_to_f32(u.x & 0xffffu);
+      oacc[db][4 * ig + 1] += p * __uint_as_float(u.x & 0xffff0000u);
+      oacc[db][4 * ig + 2] += p * bf16_bits_to_f32(u.y & 0xffffu);
+      oacc[db][4 * ig + 3] += p * __uint_as_float(u.y & 0xffff0000u);
+    }
+}
+
+// Store NB column blocks of 32 (this lane's 4-float groups of one query row).
+template <int NB>
+__device__ __forceinline__ void store_rows(float* dst, const f32x16_t* oacc) {
+#pragma unroll
+  for (int db = 0; db < NB; ++db)
 #pragma unroll
     for (int ig = 0; ig < 4; ++ig)
       *reinterpret_cast<float4*>(dst + 32 * db + 8 * ig) =
@@ -293,15 +318,31 @@ __device__ __forceinline__ void store_rows(float* dst, const f32x16_t* oacc) {
 // prompt each; with a.gen_member, member p_splits attends only to the beams'
 // generated tokens (so that work runs beside the prompt splits instead of
 // ahead of split 0). NS = LDS pipeline stages (tiles in flight + 1).
-template <int D, int NW, int NS>
-__global__ __launch_bounds__(NW * 64, 2) void shared_mfma_kernel(SharedMfmaArgs a, int64_t n_logical) {
+//
+// Key groups (KG = 2): the NW waves form KG groups of RG = NW/KG waves; each
+// group covers the same 32*RG query rows, and group kg takes the 64-key tiles
+// kg, kg+KG, ... of the range. Each step loads KG tiles (one super-tile) into
+// one LDS stage. At the end the groups' softmax states are combined through
+// LDS with the log-sum-exp rule; group kg then finalizes and stores column
+// blocks [kg*NDB/KG, (kg+1)*NDB/KG) of the head dim.
+template <int D, int NW, int NS, int KG>
+__global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(SharedMfmaArgs a,
+                                                                               int64_t n_logical) {
   // The host pass only needs this kernel's signature for its launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
   using TG = TileGeom<D>;
+  using LP = LoadPlan<D, NW, KG>;
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int LPT = 2 * LoadPlan<D, NW>::NJ;  // load instructions per tile per wave
-  __shared__ __attribute__((aligned(1024))) char smem[NS * TG::BUFB];
+  constexpr int RG = NW / KG;          // row groups of 32 query rows
+  constexpr int NDBW = NDB / KG;       // column blocks each wave finalizes
+  constexpr int ST = BN * KG;          // keys per super-tile
+  constexpr int SBUF = KG * TG::BUFB;  // LDS bytes per stage
+  constexpr int LPT = 2 * LP::NJ;      // load instructions per super-tile per wave
+  static_assert(KG == 1 || KG == 2, "one or two key groups");
+  static_assert(KG == 1 || RG * NDB * 4096 + 2 * KG * RG * 32 * 4 <= NS * SBUF,
+                "the key-group exchange must fit in the stage buffers");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * SBUF];
   __shared__ int s_last;
 
   const int64_t lb64 = xcd_logical_block(blockIdx.x, gridDim.x, n_logical);
@@ -325,6 +366,8 @@ __global__ __launch_bounds__(NW * 64, 2) void shared_mfma_kernel(SharedMfmaArgs 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int kg = __builtin_amdgcn_readfirstlane(wave / RG);
+  const int rg = wave - kg * RG;
   const int hh = lane >> 5;
   const int ql = lane & 31;
 
@@ -339,54 +382,84 @@ __global__ __launch_bounds__(NW * 64, 2) void shared_mfma_kernel(SharedMfmaArgs 
   const int kbeg = member * a.p_chunk;
   const int kend = min(P, kbeg + a.p_chunk);
   const int nkeys = __builtin_amdgcn_readfirstlane((!gen_only && kend > kbeg) ? kend - kbeg : 0);
-  const int nfull = nkeys / BN;
-  const int tail = nkeys - nfull * BN;
-  const int ntiles = nfull + (tail > 0 ? 1 : 0);
-  LoadPlan<D, NW> lp;
+  const int nsup = (nkeys + ST - 1) / ST;
+  LP lp;
   lp.init(wave, lane);
   lds_char* lsm = (lds_char*)smem;
   const int prompt_bytes = P * TG::ROWB;
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, (short)0, prompt_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, (short)0, prompt_bytes, 0x00020000);
-  // Direct HBM->LDS loads of tile t into its stage buffer. Buffer loads
+  // Direct HBM->LDS loads of super-tile t into its stage buffer. Buffer loads
   // address the prompt through descriptors bounded to its P_r rows, so keys
   // past the prompt read as zero (they are masked) and no load leaves it; the
   // only per-lane operand is the loop-invariant offset.
   auto issue_tile = [&](int t) {
-    lds_char* buf = lsm + (t % NS) * TG::BUFB;
-    const uint32_t tile_bytes = (uint32_t)((kbeg + t * BN) * TG::ROWB);
+    lds_char* buf = lsm + (t % NS) * SBUF + wave * 1024;
+    const uint32_t tile_bytes = (uint32_t)((kbeg + t * ST) * TG::ROWB);
 #pragma unroll
-    for (int j = 0; j < LoadPlan<D, NW>::NJ; ++j) {
-      const int i = wave + NW * j;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, buf + i * 1024, 16, lp.k[j], tile_bytes, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, buf + TG::TILEB + i * 1024, 16, lp.v[j], tile_bytes, 0, 0);
+    for (int j = 0; j < LP::NJ; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, buf + LP::lds_off(j), 16, lp.k[j], tile_bytes, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, buf + LP::lds_off(j) + TG::TILEB, 16, lp.v[j], tile_bytes, 0, 0);
     }
   };
-  // Tiles 0 .. NS-2 go in flight before anything else.
-  int issued = 0;
-#pragma unroll
-  for (int t = 0; t < NS - 1; ++t) {
-    if (t < ntiles) {
-      issue_tile(t);
-      issued = t + 1;
-    }
-  }
-
-  const int row = tile * (NW * 32) + wave * 32 + ql;
+  // Query rows and slot indices are requested first, so that nothing waits
+  // on the prompt tiles to reach them; super-tiles 0 .. NS-2 follow.
+  // Rows past the last query row compute on a copy of that row (their
+  // columns of S^T and O^T are independent of the others) and store nothing.
+  const int row = tile * (RG * 32) + rg * 32 + ql;
   const bool row_ok = row < M;
-  const int bq = row_ok ? row / G : 0;
-  const int gq = row_ok ? row - bq * G : 0;
+  const int rowc = min(row, M - 1);
+  const int bq = rowc / G;
+  const int gq = rowc - bq * G;
   const int64_t qrow = ((int64_t)r * s.B + bq) * s.Hq + h * G + gq;
 
   bf16x8_t qf[NDC];
   {
     const uint16_t* qp = a.q + qrow * D + 8 * hh;
 #pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (row_ok) u = *reinterpret_cast<const uint4*>(qp + 16 * dc);
-      qf[dc] = __builtin_bit_cast(bf16x8_t, u);
+    for (int dc = 0; dc < NDC; ++dc) qf[dc] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + 16 * dc));
+  }
+  // Non-Shared tokens: in the generated-token member, or (no such member) in
+  // prompt split 0. They are folded in after the prompt tiles. With one
+  // workgroup per CU (registers to spare, nothing else to hide latency
+  // behind) the slots and the first NPF tokens are fetched before the tile
+  // loop; otherwise everything is fetched after it while the CU's other
+  // workgroup computes.
+  const bool do_ns = a.k_pool != nullptr && (gen_only || (!a.gen_member && member == 0));
+  constexpr int NPF = (NS * SBUF > 80 * 1024 && NW <= 4) ? 2 : 0;
+  NonShared<D, KG> ns;
+  ns.L = 0;
+  ns.kg = kg;
+  if (do_ns) ns.init(a, r, h, bq, kg, hh);
+  // The prefetch below is branch-free (a branch would make the compiler wait
+  // for the prompt tiles before these loads): missing tokens re-read the
+  // last one, and without Non-Shared tokens every read goes to the first
+  // query row, which always exists.
+  int pslot[NPF > 0 ? NPF : 1];
+  uint4 pk[NPF > 0 ? NPF : 1][NDC];
+  uint2 pv[NPF > 0 ? NPF : 1][NDB][4];
+  if (NPF > 0) {
+    const int32_t* trow = ns.L > 0 ? ns.trow : a.prefix_len;
+    const int smask = ns.L > 0 ? -1 : 0;
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) pslot[u] = trow[max(min(kg + KG * u, ns.L - 1), 0)] & smask;
+  }
+
+  // Super-tiles 0 .. NS-2 go in flight next.
+  int issued = 0;
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t) {
+    if (t < nsup) {
+      issue_tile(t);
+      issued = t + 1;
     }
+  }
+
+  if (NPF > 0) {
+    NonShared<D, KG> pf = ns;
+    if (ns.L == 0) pf.kp = pf.vp = a.q;
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) pf.fetch(pslot[u], pk[u], pv[u]);
   }
 
   f32x16_t oacc[NDB];
@@ -396,11 +469,6 @@ __global__ __launch_bounds__(NW * 64, 2) void shared_mfma_kernel(SharedMfmaArgs 
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = neg_inf();
   float l_part = 0.f;
-
-  // Non-Shared tokens: in the generated-token member, or (no such member) in
-  // prompt split 0 while its first tiles are in flight.
-  if (a.k_pool != nullptr && (gen_only || (!a.gen_member && member == 0)))
-    nonshared_update<D>(a, r, h, bq, qf, oacc, m_run, l_part, c, hh);
 
   // Per-lane LDS byte bases. K operand (kb, dc): key 32*kb + ql, chunk
   // 2*dc + hh, at base_k ^ (32*dc) + kb*32*ROWB.
@@ -423,63 +491,140 @@ __global__ __launch_bounds__(NW * 64, 2) void shared_mfma_kernel(SharedMfmaArgs 
     vbase = TG::TILEB + key0 * TG::ROWB + 16 * (x ^ swz_v<D>(key0)) + (i16 & 1) * 8;
   }
 
-  // Wait for tile `it`, then refill the buffer tile it-1 used.
+  // Wait for super-tile `it`, then refill the buffer super-tile it-1 used.
   auto advance = [&](int it) {
     wait_tiles<LPT>(min(issued - 1 - it, NS - 2));
-    __syncthreads();  // tile `it` landed for every wave; tile it-1's buffer is free
-    if (issued < ntiles) {
+    __syncthreads();  // super-tile `it` landed for every wave; it-1's buffer is free
+    if (issued < nsup) {
       issue_tile(issued);
       ++issued;
     }
   };
-  for (int it = 0; it < nfull; ++it) {
+  // This wave's tile of super-tile `it` sits at stage (it % NS), slot kg.
+  for (int it = 0; it + 1 < nsup; ++it) {  // full super-tiles
     advance(it);
-    tile_step<D, false>(smem + (it % NS) * TG::BUFB, kbase, vbase, qf, oacc, m_run, l_part, c, hh, BN);
+    tile_step<D, false>(smem + (it % NS) * SBUF + kg * TG::BUFB, kbase, vbase, qf, oacc, m_run, l_part, c,
+                        hh, BN);
   }
-  if (tail > 0) {  // the last, partial tile of the range
-    advance(nfull);
-    tile_step<D, true>(smem + (nfull % NS) * TG::BUFB, kbase, vbase, qf, oacc, m_run, l_part, c, hh, tail);
+  if (nsup > 0) {  // the last super-tile: this wave's tile may be partial or empty
+    const int it = nsup - 1;
+    advance(it);
+    const int nv = nkeys - (it * KG + kg) * BN;
+    if (nv > 0)
+      tile_step<D, true>(smem + (it % NS) * SBUF + kg * TG::BUFB, kbase, vbase, qf, oacc, m_run, l_part, c,
+                         hh, min(nv, BN));
   }
 
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  wait_vmem();  // every tile load has landed before the stage buffers are reused
+
+  // The Non-Shared tokens: prefetched ones first, then the rest one at a time
+  // with the next slot index in flight beside each token's K/V rows.
+#pragma unroll
+  for (int u = 0; u < NPF; ++u)
+    if (ns.has(u)) token_update<D>(pk[u], pv[u], qf, oacc, m_run, l_part, c, hh);
+  if (ns.has(NPF)) {
+    int sl = ns.slot(NPF);
+    for (int u = NPF; u < NonShared<D, KG>::NT && ns.has(u); ++u) {
+      uint4 kk[NDC];
+      uint2 vv[NDB][4];
+      ns.fetch(sl, kk, vv);
+      sl = ns.slot(u + 1);
+      token_update<D>(kk, vv, qf, oacc, m_run, l_part, c, hh);
+    }
+  }
+
+  float l_tot = l_part + __shfl_xor(l_part, 32);
+  // own[j]: column block kg*NDBW + j of this wave's 32 rows, combined over
+  // the key groups.
+  f32x16_t own[NDBW];
+  if constexpr (KG == 1) {
+#pragma unroll
+    for (int j = 0; j < NDB; ++j) own[j] = oacc[j];
+  } else {
+    float4* xo = reinterpret_cast<float4*>(smem);  // [RG][NDB][4][64] float4
+    float* xm = reinterpret_cast<float*>(smem + RG * NDB * 4096);
+    float* xl = xm + KG * RG * 32;
+    __syncthreads();  // every wave is done reading the stage buffers
+    if (hh == 0) {
+      xm[(kg * RG + rg) * 32 + ql] = m_run;
+      xl[(kg * RG + rg) * 32 + ql] = l_tot;
+    }
+    // hand the other group the column blocks it finalizes
+#pragma unroll
+    for (int j = 0; j < NDBW; ++j) {
+      const int db = kg ? j : NDBW + j;
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        float4 v;
+        v.x = kg ? oacc[j][4 * ig + 0] : oacc[NDBW + j][4 * ig + 0];
+        v.y = kg ? oacc[j][4 * ig + 1] : oacc[NDBW + j][4 * ig + 1];
+        v.z = kg ? oacc[j][4 * ig + 2] : oacc[NDBW + j][4 * ig + 2];
+        v.w = kg ? oacc[j][4 * ig + 3] : oacc[NDBW + j][4 * ig + 3];
+        xo[((rg * NDB + db) * 4 + ig) * 64 + lane] = v;
+      }
+    }
+    __syncthreads();
+    const int og = ((1 - kg) * RG + rg) * 32 + ql;
+    const float mo = xm[og];
+    const float lo = xl[og];
+    const float mn = fmaxf(m_run, mo);
+    const float as = m_run == neg_inf() ? 0.f : exp2_approx(m_run - mn);
+    const float ao = mo == neg_inf() ? 0.f : exp2_approx(mo - mn);
+    l_tot = l_tot * as + lo * ao;
+    m_run = mn;
+#pragma unroll
+    for (int j = 0; j < NDBW; ++j) {
+      const int db = kg * NDBW + j;
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        const float4 v = xo[((rg * NDB + db) * 4 + ig) * 64 + lane];
+        own[j][4 * ig + 0] = (kg ? oacc[NDBW + j][4 * ig + 0] : oacc[j][4 * ig + 0]) * as + v.x * ao;
+        own[j][4 * ig + 1] = (kg ? oacc[NDBW + j][4 * ig + 1] : oacc[j][4 * ig + 1]) * as + v.y * ao;
+        own[j][4 * ig + 2] = (kg ? oacc[NDBW + j][4 * ig + 2] : oacc[j][4 * ig + 2]) * as + v.z * ao;
+        own[j][4 * ig + 3] = (kg ? oacc[NDBW + j][4 * ig + 3] : oacc[j][4 * ig + 3]) * as + v.w * ao;
+      }
+    }
+  }
+  const int dcol = 32 * NDBW * kg;  // first head-dim column this wave finalizes
+  const bool writes_lse = kg == 0 && hh == 0;
+
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   const float lse_here = l_tot > 0.f ? (m_run + log2_approx(l_tot)) * kLn2 : neg_inf();
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+  for (int j = 0; j < NDBW; ++j)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] *= inv;
+    for (int i = 0; i < 16; ++i) own[j][i] *= inv;
 
   if (a.mode == kModeFinal) {
     if (!row_ok) return;
-    store_rows<D>(a.out.o + qrow * D + 4 * hh, oacc);
-    if (a.out.lse && hh == 0) a.out.lse[qrow] = lse_here;
+    store_rows<NDBW>(a.out.o + qrow * D + dcol + 4 * hh, own);
+    if (a.out.lse && writes_lse) a.out.lse[qrow] = lse_here;
     return;
   }
   if (a.mode == kModePartial) {
     const int64_t part = a.out.part_base + member;
     if (!row_ok) return;
-    store_rows<D>(a.part_o + (part * a.part_stride + qrow) * D + 4 * hh, oacc);
-    if (hh == 0) a.part_lse[part * a.part_stride + qrow] = lse_here;
+    store_rows<NDBW>(a.part_o + (part * a.part_stride + qrow) * D + dcol + 4 * hh, own);
+    if (writes_lse) a.part_lse[part * a.part_stride + qrow] = lse_here;
     return;
   }
 
   // kModeFixup: publish this member's partial (agent-coherent), count arrivals.
   const int64_t rows = a.part_stride;
-  const int obase = (int)((qrow * D + 4 * hh) * 4);
+  const int obase = (int)((qrow * D + dcol + 4 * hh) * 4);
   {
     const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(a.part_o + (int64_t)member * rows * D, rows * D);
     const __amdgpu_buffer_rsrc_t rl = coherent_rsrc(a.part_lse + (int64_t)member * rows, rows);
     if (row_ok) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int j = 0; j < NDBW; ++j)
 #pragma unroll
         for (int ig = 0; ig < 4; ++ig) {
-          const float4 v = make_float4(oacc[db][4 * ig], oacc[db][4 * ig + 1], oacc[db][4 * ig + 2],
-                                       oacc[db][4 * ig + 3]);
+          const float4 v = make_float4(own[j][4 * ig], own[j][4 * ig + 1], own[j][4 * ig + 2], own[j][4 * ig + 3]);
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), ro,
-                                                 obase + (32 * db + 8 * ig) * 4, 0, kCoherent);
+                                                 obase + (32 * j + 8 * ig) * 4, 0, kCoherent);
         }
-      if (hh == 0)
+      if (writes_lse)
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse_here), rl, (int)(qrow * 4), 0,
                                               kCoherent);
     }
@@ -502,9 +647,9 @@ __global__ __launch_bounds__(NW * 64, 2) void shared_mfma_kernel(SharedMfmaArgs 
     lmax = fmaxf(lmax, __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, (int)(qrow * 4), 0, kCoherent)));
   }
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+  for (int j = 0; j < NDBW; ++j)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    for (int i = 0; i < 16; ++i) own[j][i] = 0.f;
   float wsum = 0.f;
   if (lmax != neg_inf()) {
     for (int sp = 0; sp < members; ++sp) {
@@ -514,36 +659,36 @@ __global__ __launch_bounds__(NW * 64, 2) void shared_mfma_kernel(SharedMfmaArgs 
       const float w = exp2_approx((lo - lmax) * kLog2e);  // empty member: exp2(-inf) = 0
       wsum += w;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int j = 0; j < NDBW; ++j)
 #pragma unroll
         for (int ig = 0; ig < 4; ++ig) {
           const float4 v = __builtin_bit_cast(
-              float4, __builtin_amdgcn_raw_buffer_load_b128(ro, obase + (32 * db + 8 * ig) * 4, 0, kCoherent));
+              float4, __builtin_amdgcn_raw_buffer_load_b128(ro, obase + (32 * j + 8 * ig) * 4, 0, kCoherent));
           if (w != 0.f) {
-            oacc[db][4 * ig + 0] += w * v.x;
-            oacc[db][4 * ig + 1] += w * v.y;
-            oacc[db][4 * ig + 2] += w * v.z;
-            oacc[db][4 * ig + 3] += w * v.w;
+            own[j][4 * ig + 0] += w * v.x;
+            own[j][4 * ig + 1] += w * v.y;
+            own[j][4 * ig + 2] += w * v.z;
+            own[j][4 * ig + 3] += w * v.w;
           }
         }
     }
   }
   const float winv = wsum > 0.f ? 1.0f / wsum : 0.f;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+  for (int j = 0; j < NDBW; ++j)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] *= winv;
-  store_rows<D>(a.out.o + qrow * D + 4 * hh, oacc);
-  if (a.out.lse && hh == 0) a.out.lse[qrow] = wsum > 0.f ? lmax + log2_approx(wsum) * kLn2 : neg_inf();
+    for (int i = 0; i < 16; ++i) own[j][i] *= winv;
+  store_rows<NDBW>(a.out.o + qrow * D + dcol + 4 * hh, own);
+  if (a.out.lse && writes_lse) a.out.lse[qrow] = wsum > 0.f ? lmax + log2_approx(wsum) * kLn2 : neg_inf();
 #endif
 }
 
-template <int D, int NW>
-hipError_t launch_dw(const SharedMfmaArgs& a, int64_t grid, int64_t n_logical, hipStream_t st) {
-  if (a.stages == 4)
-    hipLaunchKernelGGL((shared_mfma_kernel<D, NW, 4>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a, n_logical);
+template <int D, int NW, int KG>
+hipError_t launch_dwk(const SharedMfmaArgs& a, int64_t grid, int64_t n_logical, hipStream_t st) {
+  if (KG == 1 && a.stages == 4)
+    hipLaunchKernelGGL((shared_mfma_kernel<D, NW, 4, 1>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a, n_logical);
   else
-    hipLaunchKernelGGL((shared_mfma_kernel<D, NW, 2>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a, n_logical);
+    hipLaunchKernelGGL((shared_mfma_kernel<D, NW, 2, KG>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a, n_logical);
   return hipGetLastError();
 }
 
@@ -553,10 +698,17 @@ hipError_t launch_d(const SharedMfmaArgs& a, hipStream_t st) {
   const int64_t n_logical = (int64_t)a.s.R * a.s.Hkv * members * a.row_tiles;
   if (n_logical == 0) return hipSuccess;
   const int64_t grid = (n_logical + 7) / 8 * 8;
+  if (a.key_groups == 2) {
+    switch (a.waves) {
+      case 2: return launch_dwk<D, 2, 2>(a, grid, n_logical, st);
+      case 4: return launch_dwk<D, 4, 2>(a, grid, n_logical, st);
+      default: return launch_dwk<D, 8, 2>(a, grid, n_logical, st);
+    }
+  }
   switch (a.waves) {
-    case 1: return launch_dw<D, 1>(a, grid, n_logical, st);
-    case 2: return launch_dw<D, 2>(a, grid, n_logical, st);
-    default: return launch_dw<D, 4>(a, grid, n_logical, st);
+    case 1: return launch_dwk<D, 1, 1>(a, grid, n_logical, st);
+    case 2: return launch_dwk<D, 2, 1>(a, grid, n_logical, st);
+    default: return launch_dwk<D, 4, 1>(a, grid, n_logical, st);
   }
 }
 

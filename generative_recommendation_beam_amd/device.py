@@ -48,14 +48,15 @@ class DeviceWorkload:
 
 
 def upload(w: Workload, device="cuda", *, prefix_splits=0, unshared_splits=0,
-           rows_per_block=0, pipeline_stages=0, table_fill: int = -1) -> DeviceWorkload:
+           rows_per_block=0, pipeline_stages=0, key_groups=0, table_fill: int = -1) -> DeviceWorkload:
     dims = xattn.make_dims(R=w.R, B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
                            max_prefix_len=int(w.prefix_len.max()) if w.R else 0,
                            max_unshared_len=w.T_max,
                            dtype=xattn.XATTN_BF16 if w.dtype == "bf16" else xattn.XATTN_F32,
                            num_slots=w.num_slots, num_prefix_tokens=w.n_ptok, scale=w.scale,
                            prefix_splits=prefix_splits, unshared_splits=unshared_splits,
-                           rows_per_block=rows_per_block, pipeline_stages=pipeline_stages)
+                           rows_per_block=rows_per_block, pipeline_stages=pipeline_stages,
+                           key_groups=key_groups)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     T = w.T_steps
     act = np.stack([w.active(t) for t in range(T)]) if T else np.zeros((0, w.R), np.uint8)

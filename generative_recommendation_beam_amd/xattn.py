@@ -31,7 +31,7 @@ class Dims(ctypes.Structure):
                 ("num_slots", ctypes.c_int64), ("num_prefix_tokens", ctypes.c_int64),
                 ("scale", ctypes.c_float), ("prefix_splits", ctypes.c_int32),
                 ("unshared_splits", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
-                ("pipeline_stages", ctypes.c_int32)]
+                ("pipeline_stages", ctypes.c_int32), ("key_groups", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -39,7 +39,8 @@ class Plan(ctypes.Structure):
                 ("prefix_splits", ctypes.c_int32), ("prefix_chunk", ctypes.c_int32),
                 ("unshared_splits", ctypes.c_int32), ("unshared_chunk", ctypes.c_int32),
                 ("partials", ctypes.c_int32), ("mfma", ctypes.c_int32),
-                ("launches", ctypes.c_int32), ("pipeline_stages", ctypes.c_int32)]
+                ("launches", ctypes.c_int32), ("pipeline_stages", ctypes.c_int32),
+                ("key_groups", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -113,11 +114,11 @@ def _stream(stream):
 
 def make_dims(*, R, B, Hq, Hkv, D, max_prefix_len, max_unshared_len, dtype, num_slots,
               num_prefix_tokens, scale, prefix_splits=0, unshared_splits=0, rows_per_block=0,
-              pipeline_stages=0) -> Dims:
+              pipeline_stages=0, key_groups=0) -> Dims:
     return Dims(int(R), int(B), int(Hq), int(Hkv), int(D), int(max_prefix_len),
                 int(max_unshared_len), int(dtype), int(num_slots), int(num_prefix_tokens),
                 float(scale), int(prefix_splits), int(unshared_splits), int(rows_per_block),
-                int(pipeline_stages))
+                int(pipeline_stages), int(key_groups))
 
 
 def workspace_size(dims: Dims, which: int) -> int:

@@ -87,6 +87,10 @@ typedef struct {
   int32_t rows_per_block;   /* 0 = automatic; else 32, 64 or 128 query rows per
                                Shared-stage workgroup (bf16 MFMA path) */
   int32_t pipeline_stages;  /* 0 = automatic; else 2 or 4 K/V tiles staged in LDS */
+  int32_t key_groups;       /* 0 = automatic; else 1 or 2 wavefront groups per
+                               Shared-stage workgroup that take alternate 64-key
+                               tiles of the same query rows (merged in LDS);
+                               2 requires pipeline_stages 2 */
 } xattn_dims;
 
 /* Launch plan chosen for a dims (introspection for tests and tuning). */
@@ -101,6 +105,7 @@ typedef struct {
   int32_t mfma;             /* 1 = bf16 MFMA Shared stage, 0 = vector-ALU path */
   int32_t launches;         /* kernel launches per call */
   int32_t pipeline_stages;  /* K/V tiles staged in LDS (MFMA path) */
+  int32_t key_groups;       /* wavefront groups splitting each workgroup's keys */
 } xattn_plan;
 
 /*

@@ -65,6 +65,9 @@ def _decode(d, ws=None, nbytes=0, **over):
     (dict(max_unshared_len=0), xattn.XATTN_ERR_INVALID_ARG),
     (dict(scale=float("nan")), xattn.XATTN_ERR_INVALID_ARG),
     (dict(B=20000), xattn.XATTN_ERR_UNSUPPORTED),
+    (dict(key_groups=3), xattn.XATTN_ERR_INVALID_ARG),
+    (dict(key_groups=2, pipeline_stages=4), xattn.XATTN_ERR_INVALID_ARG),
+    (dict(rows_per_block=96), xattn.XATTN_ERR_INVALID_ARG),
 ])
 def test_invalid_dims_rejected(L, over, code):
     assert _decode(dims(**over)) == code
@@ -93,6 +96,11 @@ def test_plan_introspection(L):
     d = dims(R=8, B=128, Hq=16, Hkv=4, max_prefix_len=1024, max_unshared_len=3)
     p = xattn.get_plan(d, 2)
     assert p["mfma"] == 1 and p["rows_per_block"] in (32, 64, 128)
+    # 8 x 4 (request, kv head) pairs x 4 row tiles of 128 would leave CUs idle:
+    # the plan halves the rows per workgroup and splits each one's keys in two
+    assert p["key_groups"] == 2 and p["rows_per_block"] == 64 and p["row_tiles"] == 8
+    assert xattn.get_plan(dims(R=8, B=128, Hq=16, Hkv=4, max_prefix_len=1024, max_unshared_len=3,
+                               key_groups=1), 2)["rows_per_block"] == 128
     assert p["prefix_chunk"] % 64 == 0 and p["prefix_splits"] * p["prefix_chunk"] >= 1024
     assert p["unshared_splits"] == 0            # short generated tail is fused
     d2 = dims(R=4, B=16, Hq=32, Hkv=8, max_prefix_len=4096, max_unshared_len=512)
@@ -100,6 +108,9 @@ def test_plan_introspection(L):
     assert p2["unshared_splits"] > 0 and p2["partials"] == p2["prefix_splits"] + p2["unshared_splits"]
     p3 = xattn.get_plan(dims(dtype=xattn.XATTN_F32), 2)
     assert p3["mfma"] == 0
+    # enough workgroups already: one key group
+    p5 = xattn.get_plan(dims(R=16, B=256, Hq=64, Hkv=8, max_prefix_len=16384, max_unshared_len=8), 2)
+    assert p5["key_groups"] == 1 and p5["rows_per_block"] == 128
 
 
 def test_merge_argument_checks(L):

@@ -82,11 +82,31 @@ def test_decode_forced_splits(splits):
     compare(o, O, lse, L, "bf16", f"decode splits={splits} plan={plan}")
 
 
+KG_CASES = ["ragged_small_bf16", "mfma_multi_tile", "d64_bf16", "g8_bf16", "g6_bf16", "no_prefix_bf16",
+            "no_gen_bf16", "long_gen_bf16"]
+
+
+@pytest.mark.parametrize("name", KG_CASES)
+@pytest.mark.parametrize("rows,ps", [(64, 0), (128, 0), (32, 0), (64, 3)])
+def test_decode_key_groups(name, rows, ps):
+    """Two wave groups per workgroup take alternate key tiles of the same rows
+    (prompts here end inside either group's tile, or leave one group none)."""
+    w = make_workload(name, seed_key=(305, rows, ps, zlib.crc32(name.encode()) % 1000), **CASES[name])
+    d, o, lse = run_decode(w, rows_per_block=rows, key_groups=2, prefix_splits=ps)
+    plan = xattn.get_plan(d.dims, 2)
+    assert plan["mfma"] == 1 and plan["key_groups"] == 2 and plan["rows_per_block"] == rows
+    O, L = oa.attention(w)
+    compare(o, O, lse, L, w.dtype, f"decode key groups {name} plan={plan}")
+
+
 @pytest.mark.parametrize("name", ["ragged_small_bf16", "mfma_multi_tile", "b1_decode_bf16", "f32_small"])
 @pytest.mark.parametrize("ps", [0, 3])
-def test_shared_stage_matches_oracle(name, ps):
+@pytest.mark.parametrize("kg", [0, 2])
+def test_shared_stage_matches_oracle(name, ps, kg):
+    if kg and (CASES[name].get("dtype") == "f32" or name == "b1_decode_bf16"):
+        pytest.skip("vector path: no key groups")
     w = make_workload(name, seed_key=(302, ps), **CASES[name])
-    d = dv.upload(w, prefix_splits=ps)
+    d = dv.upload(w, prefix_splits=ps, key_groups=kg)
     o, lse, ws, nb = dv.alloc_outputs(d, 0)
     dv.shared_stage(d, o, lse, ws, nb)
     torch.cuda.synchronize()
