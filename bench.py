@@ -1,16 +1,26 @@
 """Benchmark: staged beam-search decode attention on one MI355X.
 
-One step = one decode step of every layer: ``xattn_decode`` on n_layers
-distinct layer buffers (distinct Q, prompt KV, Non-Shared pool and slot table
-per layer, so the working set defeats the 256 MB Infinity Cache), on
-synthetic inputs shaped like the GR semantic-ID workload by default (8
-requests, 1024-token user-history prompt, beam width 128, 3 generated tokens,
-16 q / 4 kv heads, head dim 128, bf16). Inputs are resident in HBM before the
-timed region; appends that build the Non-Shared cache happen before it.
+One step = one decode step of every layer: per layer, xattn_cache_append of
+the step's new tokens (token-granular K/V write and slot-table rewrite) and
+then xattn_decode, on n_layers distinct layer buffers (distinct Q, prompt KV,
+Non-Shared pool, slot tables and lengths per layer, so the working set
+defeats the 256 MB Infinity Cache). By default the whole step is one
+captured HIP graph (xattn_step_graph_*), launched once per step; --eager
+launches every call from the host instead. Inputs are synthetic, shaped like
+the GR semantic-ID workload by default (8 requests, 1024-token user-history
+prompt, beam width 128, 3 generated tokens, 16 q / 4 kv heads, head dim 128,
+bf16), and resident in HBM before the timed region; the cache holds every
+earlier step, and each timed step restores the lengths (one small device
+copy) and appends the last step's tokens again, so every step does the same
+work.
 
 Prints ONE JSON line. Metric: beams * layer-steps per second, plus achieved
 HBM bandwidth on algorithmic bytes (unique KV: prompt KV once per request,
-generated KV once per beam) and the roofline of the dominant kernel.
+generated KV once per beam) and the roofline of the dominant kernel (the
+decode). Its per-launch duration comes from HIP events: around every decode
+call of the timed steps with --eager; in graph mode, around K launches of a
+graph of every layer's decode, right after the timed steps (events cannot be
+recorded inside a captured graph on the runtime PyTorch ships).
 """
 from __future__ import annotations
 
@@ -56,16 +66,44 @@ def algorithmic(w):
     return dict(unique_kv=unique_kv, total=total, mfma_flops=mfma_flops, flops=all_flops)
 
 
+def _oracle_state(w):
+    """Oracle cache state before the last step's append (untimed set-up)."""
+    import numpy as np
+    from oracle import append as oapp
+    kpool = np.zeros((max(w.num_slots, 1), w.Hkv, w.D), dtype=w.k_new.dtype)
+    vpool = np.zeros_like(kpool)
+    table = np.full((w.N_b, w.T_max), -1, dtype=np.int64)
+    ulen = np.zeros(w.R, dtype=np.int64)
+    for t in range(max(w.T_steps - 1, 0)):
+        oapp.cache_append(B=w.B, k_new=w.k_new[t], v_new=w.v_new[t], parent=w.parents[t],
+                          slot_base=w.slot_base, active=w.active(t), k_pool=kpool, v_pool=vpool,
+                          table_in=table, table_out=table, unshared_len=ulen)
+    return kpool, vpool, table, ulen
+
+
 def cpu_baseline(layers_np, min_seconds=10.0):
-    """Time the oracle (as it stands) on whole layers until min_seconds pass."""
+    """Time the oracle (as it stands) on whole layer steps, the append of the
+    last step's tokens plus the decode attention, until min_seconds pass."""
+    from oracle import append as oapp
     from oracle import pool
+    states = [_oracle_state(w) for w in layers_np]
     done_beams = 0
     done_layers = 0
-    t0 = time.perf_counter()
     workers = pool.host_cores()
+    used = workers
+    t0 = time.perf_counter()
     i = 0
     while True:
         w = layers_np[i % len(layers_np)]
+        kpool, vpool, table, ulen = states[i % len(layers_np)]
+        if w.T_steps > 0:
+            t = w.T_steps - 1
+            u0 = ulen.copy()
+            tout = table.copy()
+            oapp.cache_append(B=w.B, k_new=w.k_new[t], v_new=w.v_new[t], parent=w.parents[t],
+                              slot_base=w.slot_base, active=w.active(t), k_pool=kpool, v_pool=vpool,
+                              table_in=table, table_out=tout, unshared_len=ulen)
+            ulen[:] = u0
         _, _, dt, used = pool.attention_parallel(w, workers=workers)
         done_beams += w.N_b
         done_layers += 1
@@ -74,8 +112,19 @@ def cpu_baseline(layers_np, min_seconds=10.0):
             break
     el = time.perf_counter() - t0
     return dict(value=done_beams / el, unit="beams*layer-steps/s", cores=used, kind="oracle",
-                sample=f"{done_layers} full layer decode steps of the same workload "
-                       f"(fp64 numpy oracle, {used} worker processes, {el:.1f} s)")
+                sample=f"{done_layers} full layer steps (append of the last step's tokens + decode) "
+                       f"of the same workload (fp64 numpy oracle, {used} worker processes, {el:.1f} s)")
+
+
+def append_bytes(w):
+    """Algorithmic bytes of one layer's append of the last step's tokens."""
+    e = w.elem_bytes
+    if w.T_steps == 0:
+        return 0
+    t = w.T_steps - 1
+    act = w.active(t)
+    beams = int(sum(w.B for r in range(w.R) if act[r]))
+    return 2 * 2 * beams * w.Hkv * w.D * e + 2 * beams * t * 4 + beams * 4
 
 
 KERNEL_SOURCES = ("generative_recommendation_beam_amd/csrc/shared_mfma.hip",
@@ -134,6 +183,8 @@ def main():
     ap.add_argument("--rows-per-block", type=int, default=0, help="override rows per workgroup (0 = auto)")
     ap.add_argument("--stages", type=int, default=0, help="override LDS pipeline stages (0 = auto)")
     ap.add_argument("--key-groups", type=int, default=0, help="override key groups per workgroup (0 = auto)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every call from the host instead of one captured step graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -161,46 +212,91 @@ def main():
     n_layers = args.layers or DEFAULT_LAYERS[str(cfg)]
 
     layers_np = [inputs.config(cfg, layer=l) for l in range(n_layers)]
+    w0 = layers_np[0]
+    # One [n_layers][R] length array, restored with one copy per step.
+    ulen_all = torch.zeros((n_layers, max(w0.R, 1)), dtype=torch.int32, device="cuda")
     layers = []
-    for w in layers_np:
+    for l, w in enumerate(layers_np):
         d = dv.upload(w, prefix_splits=args.prefix_splits, rows_per_block=args.rows_per_block,
                       pipeline_stages=args.stages, key_groups=args.key_groups)
-        dv.build_cache(d)
+        d.unshared_len = ulen_all[l]
+        table_in, table_out, t_last = dv.prepare_step(d)
         o, lse, ws, nb = dv.alloc_outputs(d, 2)
-        layers.append((d, o, lse, ws, nb))
+        layers.append((d, o, lse, ws, nb, table_in, table_out, t_last))
+    ulen0 = ulen_all.clone()
     torch.cuda.synchronize()
-    w0 = layers_np[0]
     plan = xattn.get_plan(layers[0][0].dims, 2)
     alg = algorithmic(w0)
+    K = args.steps
 
-    def one_step(evs=None):
-        for i, (d, o, lse, ws, nb) in enumerate(layers):
-            if evs is not None:
-                evs[i][0].record()
-            dv.decode(d, o, lse, ws, nb)
-            if evs is not None:
-                evs[i][1].record()
+    def new_events():
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in layers]
+
+    def eager_step(evs):
+        ulen_all.copy_(ulen0)
+        for (d, o, lse, ws, nb, tin, tout, t_last), (e0, e1) in zip(layers, evs):
+            if t_last is not None:
+                dv.append_step(d, t_last, table_in=tin, table_out=tout)
+            e0.record()
+            xattn.decode(d.dims, d.q, d.k_shared, d.v_shared, d.prefix_off, d.prefix_len, d.k_pool,
+                         d.v_pool, tout, d.unshared_len, o, lse, ws if nb else None, nb)
+            e1.record()
+
+    step_evs = [new_events() for _ in range(K)] if args.eager else []
+    warm_evs = new_events()
+    if not args.eager:
+        # The whole step (every layer's append and decode) as one graph.
+        step_graph = xattn.StepGraph([dv.layer_step(d, o, lse, ws, nb, tin, tout, t_last)
+                                      for (d, o, lse, ws, nb, tin, tout, t_last) in layers])
+        # Every layer's decode alone, back to back in one graph, to time the
+        # decode kernel with HIP events around its launches (the runtime
+        # PyTorch ships cannot record events inside a captured graph).
+        decode_graph = xattn.StepGraph([dv.layer_step(d, o, lse, ws, nb, None, tout, None)
+                                        for (d, o, lse, ws, nb, tin, tout, t_last) in layers])
+        torch.cuda.synchronize()
+
+    def one_step(k):
+        if args.eager:
+            eager_step(warm_evs if k < 0 else step_evs[k])
+        else:
+            ulen_all.copy_(ulen0)
+            step_graph.launch()
 
     for _ in range(args.warmup):
-        one_step()
+        one_step(-1)
     torch.cuda.synchronize()
 
-    K = args.steps
-    call_evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-                 for _ in layers] for _ in range(K)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for k in range(K):
-        one_step(call_evs[k])
+        one_step(k)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
-    call_ms = np.array([[e[0].elapsed_time(e[1]) for e in step] for step in call_evs])
-    call_us = float(call_ms.mean() * 1e3)
+    if args.eager:
+        call_ms = np.array([[e0.elapsed_time(e1) for (e0, e1) in evs] for evs in step_evs])
+        call_us = float(call_ms.mean() * 1e3)
+    else:
+        # Kernel timing pass, right after the timed steps, on the state they
+        # leave (every layer's cache complete): K launches of the graph of
+        # every layer's decode, each between two HIP events on the launch
+        # stream; a decode's duration is the pair's interval / n_layers
+        # (back-to-back kernels of one graph: only graph-internal gaps added).
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(K)]
+        for e0, e1 in pairs:
+            e0.record()
+            decode_graph.launch()
+            e1.record()
+        torch.cuda.synchronize()
+        call_us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in pairs]) * 1e3 / n_layers)
+        step_graph.close()
+        decode_graph.close()
 
     ms_per_step = ms_total / K
     value = w0.N_b * n_layers / (ms_per_step / 1e3)
@@ -217,6 +313,9 @@ def main():
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=peak_tflops, unit="TFLOP/s",
                     frac=round(achieved / peak_tflops, 4), traffic=measured_traffic(cfg))
     roof["kernel"] = "xattn_decode call (%d kernel launch%s)" % (plan["launches"], "" if plan["launches"] == 1 else "es")
+    roof["timing"] = ("HIP events around K launches of a graph of the n_layers decodes (interval / "
+                      "n_layers), run right after the timed steps" if not args.eager else
+                      "HIP events around every decode call of the timed steps")
     roof["avg_call_us"] = round(call_us, 3)
     roof["algorithmic_bytes_per_call"] = alg["total"]
     roof["algorithmic_mfma_flops_per_call"] = alg["mfma_flops"]
@@ -236,11 +335,13 @@ def main():
         "dtype": w0.dtype,
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[str(cfg)], "n_layers": n_layers,
-                   "beams_per_call": w0.N_b, "plan": plan},
+                   "beams_per_call": w0.N_b, "step": "append + decode per layer",
+                   "launch": "eager" if args.eager else "graph", "plan": plan},
         "unique_kv_GBps": round(alg["unique_kv"] / call_s / 1e9, 1),
         "total_GBps": round(alg["total"] / call_s / 1e9, 1),
         "mfma_TFLOPs": round(alg["mfma_flops"] / call_s / 1e12, 1),
         "wall_s_timed": round(wall, 4),
+        "step_GBps": round(n_layers * (alg["total"] + append_bytes(w0)) / (ms_per_step * 1e-3) / 1e9, 1),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -1,6 +1,6 @@
 // C-ABI entry points: host-side validation, launch planning, workspace
 // layout and dispatch. Nothing is enqueued unless every host-checkable
-// argument is valid. The library never allocates, frees or synchronizes.
+// argument is valid. These entry points never allocate, free or synchronize.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -482,6 +482,7 @@ xattn_status xattn_cache_append(const xattn_dims* d, const void* k_new, const vo
   a.table_in = table_in;
   a.table_out = table_out;
   a.unshared_len = ulen;
+  if (!append_supported(a)) return XATTN_ERR_UNSUPPORTED;
   return hip_status(launch_append(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -98,6 +98,12 @@ struct AppendArgs {
   int32_t* table_out;
   int32_t* unshared_len;
 };
+// One launch per append; its workgroups count their arrivals in the bits of
+// unshared_len[r] from kArrivalShift up, so lengths stay below 2^kArrivalShift
+// and a request has at most kMaxAppendBlocks workgroups.
+constexpr int kArrivalShift = 20;
+constexpr int kMaxAppendBlocks = 2047;
+bool append_supported(const AppendArgs& a);
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 
 }  // namespace xattn

@@ -112,3 +112,32 @@ def shared_stage(d: DeviceWorkload, o, lse, ws, nbytes, stream=None):
 def unshared_stage(d: DeviceWorkload, o, lse, ws, nbytes, stream=None):
     xattn.unshared_stage(d.dims, d.q, d.k_pool, d.v_pool, d.table, d.unshared_len, o, lse,
                          ws if nbytes else None, nbytes, stream=stream)
+
+
+def prepare_step(d: DeviceWorkload):
+    """Cache state one step before the end: every decode step but the last is
+    appended (in place into d.table). Returns (table_in, table_out, t_last):
+    the step appends step t_last's tokens from table_in into table_out and
+    decodes on table_out; t_last is None when there are no generated tokens.
+    Restoring d.unshared_len to its value here makes the step repeatable."""
+    T = d.w.T_steps
+    for t in range(max(T - 1, 0)):
+        append_step(d, t)
+    table_out = d.table.clone()
+    return d.table, table_out, (T - 1 if T > 0 else None)
+
+
+def layer_step(d: DeviceWorkload, o, lse, ws, nbytes, table_in, table_out, t_last,
+               decode_begin=None, decode_end=None):
+    """xattn_layer_step of one layer: append step t_last (if any), then decode."""
+    app = {}
+    if t_last is not None:
+        app = dict(k_new=d.k_new[t_last], v_new=d.v_new[t_last], parent=d.parents[t_last],
+                   slot_base=d.slot_base, active=d.active[t_last], table_in=table_in)
+    return xattn.layer_step(d.dims, q=d.q, k_shared=d.k_shared, v_shared=d.v_shared,
+                            prefix_off=d.prefix_off, prefix_len=d.prefix_len, k_pool=d.k_pool,
+                            v_pool=d.v_pool, table_out=table_out, unshared_len=d.unshared_len,
+                            o=o, lse=lse, workspace=ws if nbytes else None,
+                            workspace_bytes=nbytes, decode_begin=decode_begin,
+                            decode_end=decode_end, **app)
+

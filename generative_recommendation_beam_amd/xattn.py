@@ -20,7 +20,8 @@ XATTN_OK, XATTN_ERR_INVALID_ARG, XATTN_ERR_UNSUPPORTED, XATTN_ERR_WORKSPACE, XAT
 XATTN_F32, XATTN_BF16 = 0, 1
 
 EXPORTED = ("xattn_workspace_size", "xattn_get_plan", "xattn_shared_stage", "xattn_unshared_stage",
-            "xattn_merge", "xattn_decode", "xattn_cache_append", "xattn_status_string")
+            "xattn_merge", "xattn_decode", "xattn_cache_append", "xattn_step_graph_create",
+            "xattn_step_graph_launch", "xattn_step_graph_destroy", "xattn_status_string")
 
 
 class Dims(ctypes.Structure):
@@ -44,6 +45,19 @@ class Plan(ctypes.Structure):
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+P_ = ctypes.c_void_p
+
+
+class LayerStep(ctypes.Structure):
+    """One layer of a captured decode step (xattn_layer_step)."""
+    _fields_ = [("dims", Dims), ("k_new", P_), ("v_new", P_), ("parent", P_), ("slot_base", P_),
+                ("active", P_), ("table_in", P_), ("table_out", P_), ("unshared_len", P_),
+                ("q", P_), ("k_shared", P_), ("v_shared", P_), ("prefix_off", P_),
+                ("prefix_len", P_), ("k_pool", P_), ("v_pool", P_), ("o", P_), ("lse", P_),
+                ("workspace", P_), ("workspace_bytes", ctypes.c_size_t), ("decode_begin", P_),
+                ("decode_end", P_)]
 
 
 class XattnError(RuntimeError):
@@ -83,6 +97,13 @@ def lib():
     L.xattn_decode.argtypes = [pd, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     L.xattn_cache_append.restype = ctypes.c_int
     L.xattn_cache_append.argtypes = [pd, P, P, P, P, P, P, P, P, P, P, P]
+    L.xattn_step_graph_create.restype = ctypes.c_int
+    L.xattn_step_graph_create.argtypes = [ctypes.POINTER(LayerStep), ctypes.c_int32,
+                                          ctypes.POINTER(ctypes.c_void_p)]
+    L.xattn_step_graph_launch.restype = ctypes.c_int
+    L.xattn_step_graph_launch.argtypes = [P, P]
+    L.xattn_step_graph_destroy.restype = ctypes.c_int
+    L.xattn_step_graph_destroy.argtypes = [P]
     _lib = L
     return L
 
@@ -172,3 +193,52 @@ def cache_append(dims, k_new, v_new, parent, slot_base, active, k_pool, v_pool, 
                                     _ptr(table_in), _ptr(table_out), _ptr(unshared_len),
                                     _stream(stream)),
            "xattn_cache_append")
+
+
+def layer_step(dims, *, q, k_shared, v_shared, prefix_off, prefix_len, k_pool, v_pool, table_out,
+               unshared_len, o, lse=None, workspace=None, workspace_bytes=0, k_new=None, v_new=None,
+               parent=None, slot_base=None, active=None, table_in=None, decode_begin=None,
+               decode_end=None) -> LayerStep:
+    """Fill one xattn_layer_step from tensors (events: objects whose
+    `cuda_event` is a hipEvent_t handle, or None).
+
+    The returned object keeps every tensor and event it points to alive; a
+    StepGraph keeps its LayerSteps, so a captured graph never refers to memory
+    that was freed (and possibly handed to another tensor) behind it."""
+    ev = lambda e: None if e is None else e.cuda_event
+    st = LayerStep(dims, _ptr(k_new), _ptr(v_new), _ptr(parent), _ptr(slot_base), _ptr(active),
+                   _ptr(table_in), _ptr(table_out), _ptr(unshared_len), _ptr(q), _ptr(k_shared),
+                   _ptr(v_shared), _ptr(prefix_off), _ptr(prefix_len), _ptr(k_pool), _ptr(v_pool),
+                   _ptr(o), _ptr(lse), _ptr(workspace), int(workspace_bytes), ev(decode_begin),
+                   ev(decode_end))
+    st.keep_alive = [x for x in (k_new, v_new, parent, slot_base, active, table_in, table_out,
+                                 unshared_len, q, k_shared, v_shared, prefix_off, prefix_len, k_pool,
+                                 v_pool, o, lse, workspace, decode_begin, decode_end)
+                     if x is not None and not isinstance(x, int)]
+    return st
+
+
+class StepGraph:
+    """A captured multi-layer decode step (xattn_step_graph_*)."""
+
+    def __init__(self, steps):
+        self._steps = list(steps)  # their keep_alive lists pin the graph's buffers
+        arr = (LayerStep * len(steps))(*steps)
+        h = ctypes.c_void_p(None)
+        _check(lib().xattn_step_graph_create(arr, len(steps), ctypes.byref(h)),
+               "xattn_step_graph_create")
+        self._h = h
+
+    def launch(self, stream=None):
+        _check(lib().xattn_step_graph_launch(self._h, _stream(stream)), "xattn_step_graph_launch")
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            _check(lib().xattn_step_graph_destroy(self._h), "xattn_step_graph_destroy")
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

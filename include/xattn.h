@@ -17,9 +17,10 @@
  *
  * CONVENTIONS
  *  - Every pointer argument named as device memory must point to memory the
- *    caller allocated on the current HIP device. The library never allocates,
- *    frees or synchronizes; it only enqueues kernels on `stream` (a
- *    hipStream_t; NULL = the null stream) and returns.
+ *    caller allocated on the current HIP device. Apart from the step-graph
+ *    create/destroy calls, the library never allocates, frees or
+ *    synchronizes; it only enqueues kernels on `stream` (a hipStream_t;
+ *    NULL = the null stream) and returns.
  *  - Every condition the host can check is checked before anything is
  *    launched; on error nothing is enqueued. The contents of device arrays
  *    (lengths, offsets, slot indices, parents) are trusted: out-of-range
@@ -180,8 +181,8 @@ xattn_status xattn_decode(const xattn_dims* dims, const void* q, const void* k_s
  * In-place token-granular append of one decode step (xGR page, section 2.1,
  * in-place updates through direct indices without read-before-write
  * hazards; section 1, block copies on branching are what this avoids).
- * For every request r with active[r] != 0 (active may be NULL = all), with
- * t = unshared_len[r] (must be < max_unshared_len) and every new beam b:
+ * For every request r with active[r] != 0 (active may be NULL = all) and
+ * t = unshared_len[r] < max_unshared_len, and every new beam b:
  *   slot                  = slot_base[r] + t*B + b
  *   k_pool[slot], v_pool[slot] <- k_new[r*B + b], v_new[r*B + b]   ([H_kv][D] each)
  *   table_out[r*B+b][0..t) <- table_in[r*B + parent[r*B+b]][0..t)  (t > 0 only)
@@ -193,13 +194,82 @@ xattn_status xattn_decode(const xattn_dims* dims, const void* q, const void* k_s
  * k_new / v_new: [N_b][H_kv][D] (dims.dtype); parent [N_b] int32;
  * slot_base [R] int64; active [R] uint8 or NULL; tables [N_b][T_max] int32;
  * unshared_len [R] int32 (read, then incremented). Needs no workspace.
- * Slots must lie in [0, num_slots).
+ * Slots must lie in [0, num_slots). A request whose row is full
+ * (t == max_unshared_len) is left unchanged.
+ * One kernel launch: while it runs, its workgroups count their arrivals in
+ * bits 20 and up of unshared_len, so lengths must stay below 2^20 and nothing
+ * else may read unshared_len during the call. XATTN_ERR_UNSUPPORTED if
+ * max_unshared_len >= 2^20 or one request would need more than 2047
+ * workgroups (very large beam_width * max_unshared_len).
  */
 xattn_status xattn_cache_append(const xattn_dims* dims, const void* k_new, const void* v_new,
                                 const int32_t* parent, const int64_t* slot_base,
                                 const uint8_t* active, void* k_pool, void* v_pool,
                                 const int32_t* table_in, int32_t* table_out,
                                 int32_t* unshared_len, void* stream);
+
+/*
+ * Multi-layer decode step as one HIP graph (xGR page, section 2.3 xSchedule:
+ * device work is captured once into a static graph and submitted as a whole,
+ * cutting kernel-launch overhead and CPU involvement; the xLLM page's engine
+ * layer does the same with dimension parameters and reports a throughput
+ * gain for smaller models in its ablations). At the GR decode sizes the
+ * per-call host launch path costs more than the kernel itself.
+ *
+ * Each layer is self-contained: its own pool, slot tables and lengths. The
+ * step runs, for every layer in order, xattn_cache_append (skipped when
+ * k_new is NULL) and then xattn_decode on the table the append wrote
+ * (table_out), with the arguments below exactly as those calls take them.
+ * Positions are read from device memory when the graph runs, so one graph
+ * serves every decode step: refill q / k_new / v_new / parent in place and
+ * launch it again. If decode_begin / decode_end are not NULL (hipEvent_t
+ * created with timing enabled), they are captured as external event-record
+ * nodes around the layer's decode, recorded on every launch; a HIP runtime
+ * that cannot capture external event records (the one PyTorch 2.10 ships
+ * for ROCm 7.0 cannot) makes the create call fail with XATTN_ERR_HIP.
+ */
+typedef struct {
+  xattn_dims dims;
+  const void* k_new;         /* NULL: no append in this layer */
+  const void* v_new;
+  const int32_t* parent;
+  const int64_t* slot_base;
+  const uint8_t* active;
+  const int32_t* table_in;
+  int32_t* table_out;        /* also the decode's slot table */
+  int32_t* unshared_len;
+  const void* q;
+  const void* k_shared;
+  const void* v_shared;
+  const int64_t* prefix_off;
+  const int32_t* prefix_len;
+  void* k_pool;
+  void* v_pool;
+  float* o;
+  float* lse;                /* may be NULL */
+  void* workspace;
+  size_t workspace_bytes;
+  void* decode_begin;        /* hipEvent_t or NULL */
+  void* decode_end;          /* hipEvent_t or NULL */
+} xattn_layer_step;
+
+typedef struct xattn_step_graph xattn_step_graph;  /* opaque */
+
+/*
+ * Capture the step for n_layers >= 1 layers and instantiate it. Every
+ * argument is validated as the eager calls validate theirs; on any error
+ * nothing is kept and *graph is left NULL. This call (and only this one, with
+ * destroy) allocates: the graph, its executable form and a capture stream.
+ * XATTN_ERR_HIP if capture or instantiation fails.
+ */
+xattn_status xattn_step_graph_create(const xattn_layer_step* layers, int32_t n_layers,
+                                     xattn_step_graph** graph);
+/* Enqueue one step on `stream`. The graph's buffers must not be in use by
+ * other work on other streams meanwhile. */
+xattn_status xattn_step_graph_launch(xattn_step_graph* graph, void* stream);
+/* Release the graph (NULL is allowed). The caller makes sure no launch of it
+ * is still running. */
+xattn_status xattn_step_graph_destroy(xattn_step_graph* graph);
 
 /* Human-readable name of a status code (static storage). */
 const char* xattn_status_string(xattn_status status);

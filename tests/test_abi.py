@@ -124,6 +124,8 @@ def test_append_argument_checks(L):
     d = dims()
     f = L.xattn_cache_append
     assert f(ctypes.byref(d), None, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == xattn.XATTN_ERR_INVALID_ARG
+    d3 = dims(max_unshared_len=1 << 20)  # lengths share their int with an arrival count
+    assert f(ctypes.byref(d3), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == xattn.XATTN_ERR_UNSUPPORTED
     d2 = dims(num_slots=3)   # fewer slots than beams
     assert f(ctypes.byref(d2), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == xattn.XATTN_ERR_INVALID_ARG
 
@@ -146,3 +148,15 @@ def test_library_has_no_undefined_internal_symbols(L):
                          text=True, check=True).stdout
     bad = [l for l in out.splitlines() if "xattn" in l]
     assert not bad, bad
+
+
+def test_step_graph_argument_checks(L):
+    """Rejected before any stream or graph is made (no GPU needed)."""
+    h = ctypes.c_void_p(None)
+    assert L.xattn_step_graph_create(None, 1, ctypes.byref(h)) == xattn.XATTN_ERR_INVALID_ARG
+    arr = (xattn.LayerStep * 1)()
+    assert L.xattn_step_graph_create(arr, 0, ctypes.byref(h)) == xattn.XATTN_ERR_INVALID_ARG
+    assert L.xattn_step_graph_create(arr, 1, None) == xattn.XATTN_ERR_INVALID_ARG
+    assert not h.value
+    assert L.xattn_step_graph_launch(None, None) == xattn.XATTN_ERR_INVALID_ARG
+    assert L.xattn_step_graph_destroy(None) == xattn.XATTN_OK

@@ -223,6 +223,28 @@ def test_append_large_beam_column_chunks():
     kpool, vpool, table, ulen = _oracle_append(w)
     assert np.array_equal(_np(d.table).astype(np.int64), table)
     assert np.array_equal(_np(d.unshared_len)[:w.R], ulen)
+    kp = _np(d.k_pool.view(torch.int16)).view(np.uint16)
+    vp = _np(d.v_pool.view(torch.int16)).view(np.uint16)
+    assert np.array_equal(kp, kpool) and np.array_equal(vp, vpool)
+
+
+def test_append_on_full_row_changes_nothing():
+    """An append on requests whose rows are full writes nothing and leaves the
+    lengths as they are (every workgroup still arrives once)."""
+    w = make_workload("full", R=3, B=24, Hq=4, Hkv=2, D=128, prefix_len=1, unshared_len=[4, 4, 2],
+                      seed_key=(310, 0), T_max=4)
+    d = dv.upload(w)
+    dv.build_cache(d)
+    torch.cuda.synchronize()
+    before = [_np(x).copy() for x in (d.unshared_len, d.table, d.k_pool.view(torch.int16), d.v_pool.view(torch.int16))]
+    active = torch.tensor([1, 1, 0], dtype=torch.uint8, device=d.q.device)
+    xattn.cache_append(d.dims, d.k_new[0], d.v_new[0], d.parents[1], d.slot_base, active, d.k_pool, d.v_pool,
+                       d.table, d.table, d.unshared_len)
+    torch.cuda.synchronize()
+    after = [_np(x) for x in (d.unshared_len, d.table, d.k_pool.view(torch.int16), d.v_pool.view(torch.int16))]
+    for b, a in zip(before, after):
+        assert np.array_equal(b, a)
+    assert list(after[0][:3]) == [4, 4, 2]
 
 
 def test_decode_identical_histories_bitwise():
