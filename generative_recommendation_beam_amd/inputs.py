@@ -272,3 +272,82 @@ def as_distinct_prefixes(w: Workload, name: str) -> Workload:
                     parents=np.zeros_like(w.parents),
                     slot_base=np.arange(N_b, dtype=np.int64) * T_max,
                     num_slots=N_b * T_max, meta=dict(w.meta, derived_from=w.name))
+
+
+@dataclass
+class TopKInput:
+    """One decode step's beam-search candidate pools, per request.
+
+    beam_score [R][BW] f32: cumulative log-probability of each live beam
+    (descending in b, as the previous selection leaves them); logprob
+    [R][BW][K] f32: each beam's K best next-token log-probabilities, sorted
+    descending along K (equal values keep their vocabulary order); token
+    [R][BW][K] int32: the matching token ids; n_out: beams to keep.
+    """
+    name: str
+    beam_score: np.ndarray
+    logprob: np.ndarray
+    token: np.ndarray
+    n_out: int
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def R(self) -> int:
+        return int(self.logprob.shape[0])
+
+    @property
+    def BW(self) -> int:
+        return int(self.logprob.shape[1])
+
+    @property
+    def K(self) -> int:
+        return int(self.logprob.shape[2])
+
+
+def make_topk(name: str, *, R: int, BW: int, K: int, n_out: Optional[int] = None,
+              seed_key=(0, 0), dist: str = "softmax", vocab: int = 8192, step: int = 3,
+              logit_std: float = 2.0) -> TopKInput:
+    """Seeded candidate pools.
+
+    dist:
+      "softmax": per beam, logits ~ N(0, logit_std^2) over `vocab` tokens,
+                 log-softmax (float64, then float32), the K largest kept in
+                 descending order; beam scores are the sum of `step` earlier
+                 such picks plus noise, sorted descending;
+      "ties":    like softmax, but log-probs and beam scores are rounded to
+                 multiples of 1/4 so that many candidate scores tie exactly;
+      "masked":  like softmax, with a random tail of each beam set to -inf
+                 (tokens a validity mask removed);
+      "equal":   every log-prob and beam score is the same value.
+    """
+    n_out = BW if n_out is None else n_out
+    rng = np.random.default_rng(np.random.SeedSequence([0x70B, *[int(x) for x in seed_key]]))
+    if dist == "equal":
+        lp = np.full((R, BW, K), -1.5, dtype=np.float32)
+        bs = np.full((R, BW), -4.0, dtype=np.float32)
+        tok = np.broadcast_to(np.arange(K, dtype=np.int32), (R, BW, K)).copy()
+        return TopKInput(name, bs, lp, tok, n_out, dict(dist=dist))
+    lp = np.empty((R, BW, K), dtype=np.float32)
+    tok = np.empty((R, BW, K), dtype=np.int32)
+    for r in range(R):
+        logits = rng.standard_normal(size=(BW, vocab)) * logit_std
+        logits -= logits.max(axis=1, keepdims=True)
+        lsm = logits - np.log(np.exp(logits).sum(axis=1, keepdims=True))
+        order = np.argsort(-lsm, axis=1, kind="stable")[:, :K]
+        lp[r] = np.take_along_axis(lsm, order, axis=1).astype(np.float32)
+        tok[r] = order.astype(np.int32)
+    base = np.float32(step) * lp[:, :, 0].mean(axis=1, keepdims=True)
+    bs = (base + rng.standard_normal(size=(R, BW)).astype(np.float32)).astype(np.float32)
+    bs = -np.sort(-bs, axis=1)
+    if dist == "ties":
+        # rounding is monotone, so each beam's row stays sorted (with ties)
+        lp = (np.round(lp * 4.0) / 4.0).astype(np.float32)
+        bs = (np.round(bs * 4.0) / 4.0).astype(np.float32)
+    elif dist == "masked":
+        cut = rng.integers(1, K + 1, size=(R, BW))
+        for r in range(R):
+            for b in range(BW):
+                lp[r, b, cut[r, b]:] = -np.inf
+    elif dist != "softmax":
+        raise ValueError(dist)
+    return TopKInput(name, bs.astype(np.float32), lp, tok, n_out, dict(dist=dist))

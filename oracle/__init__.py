@@ -11,6 +11,8 @@ Modules:
              (prompt + generated-history) key sequence; stage special cases;
              log-sum-exp merge.
   append     reference semantics of the token-granular cache update.
+  beam_topk  reference semantics of beam-search survivor selection (the n_out
+             best candidates by score, index tie-break).
   pool       process-pool driver used to time the oracle on many cores.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against brute force,
