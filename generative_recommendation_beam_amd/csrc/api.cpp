@@ -486,4 +486,28 @@ xattn_status xattn_cache_append(const xattn_dims* d, const void* k_new, const vo
   return hip_status(launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
+xattn_status xattn_beam_topk(int32_t num_requests, int32_t beam_width, int32_t top_k, int32_t n_out,
+                             const float* beam_score, const float* logprob, const int32_t* token,
+                             int32_t* parent, int32_t* token_out, float* score_out, void* stream) {
+  if (num_requests < 0 || beam_width < 1 || top_k < 1 || n_out < 0) return XATTN_ERR_INVALID_ARG;
+  if ((int64_t)beam_width * top_k < n_out) return XATTN_ERR_INVALID_ARG;
+  if (num_requests == 0 || n_out == 0) return XATTN_OK;
+  if (!beam_score || !logprob || !token || !parent || !token_out || !score_out)
+    return XATTN_ERR_INVALID_ARG;
+  if (beam_width > kTopkMaxBeams || n_out > kTopkMaxOut || top_k > kTopkCap - n_out)
+    return XATTN_ERR_UNSUPPORTED;
+  TopkArgs a;
+  a.R = num_requests;
+  a.BW = beam_width;
+  a.K = top_k;
+  a.n_out = n_out;
+  a.beam_score = beam_score;
+  a.logprob = logprob;
+  a.token = token;
+  a.parent = parent;
+  a.token_out = token_out;
+  a.score_out = score_out;
+  return hip_status(launch_beam_topk(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -106,4 +106,19 @@ constexpr int kMaxAppendBlocks = 2047;
 bool append_supported(const AppendArgs& a);
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 
+// ---- Beam-search survivor selection (topk.hip) ----
+constexpr int kTopkCap = 8192;        // candidate keys held in LDS per request
+constexpr int kTopkMaxBeams = 8192;   // beams per request
+constexpr int kTopkMaxOut = 4096;     // survivors per request
+struct TopkArgs {
+  int R, BW, K, n_out;
+  const float* beam_score;  // [R][BW]
+  const float* logprob;     // [R][BW][K], each row descending
+  const int32_t* token;     // [R][BW][K]
+  int32_t* parent;          // [R][n_out]
+  int32_t* token_out;       // [R][n_out]
+  float* score_out;         // [R][n_out]
+};
+hipError_t launch_beam_topk(const TopkArgs& a, hipStream_t st);
+
 }  // namespace xattn

@@ -20,7 +20,8 @@ XATTN_OK, XATTN_ERR_INVALID_ARG, XATTN_ERR_UNSUPPORTED, XATTN_ERR_WORKSPACE, XAT
 XATTN_F32, XATTN_BF16 = 0, 1
 
 EXPORTED = ("xattn_workspace_size", "xattn_get_plan", "xattn_shared_stage", "xattn_unshared_stage",
-            "xattn_merge", "xattn_decode", "xattn_cache_append", "xattn_step_graph_create",
+            "xattn_merge", "xattn_decode", "xattn_cache_append", "xattn_beam_topk",
+            "xattn_step_graph_create",
             "xattn_step_graph_launch", "xattn_step_graph_destroy", "xattn_status_string")
 
 
@@ -97,6 +98,9 @@ def lib():
     L.xattn_decode.argtypes = [pd, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     L.xattn_cache_append.restype = ctypes.c_int
     L.xattn_cache_append.argtypes = [pd, P, P, P, P, P, P, P, P, P, P, P]
+    L.xattn_beam_topk.restype = ctypes.c_int
+    L.xattn_beam_topk.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  P, P, P, P, P, P, P]
     L.xattn_step_graph_create.restype = ctypes.c_int
     L.xattn_step_graph_create.argtypes = [ctypes.POINTER(LayerStep), ctypes.c_int32,
                                           ctypes.POINTER(ctypes.c_void_p)]
@@ -193,6 +197,14 @@ def cache_append(dims, k_new, v_new, parent, slot_base, active, k_pool, v_pool, 
                                     _ptr(table_in), _ptr(table_out), _ptr(unshared_len),
                                     _stream(stream)),
            "xattn_cache_append")
+
+
+def beam_topk(beam_score, logprob, token, n_out, parent, token_out, score_out, stream=None):
+    """beam_score [R][BW], logprob / token [R][BW][K] -> parent / token_out / score_out [R][n_out]."""
+    R, BW, K = (int(x) for x in logprob.shape)
+    _check(lib().xattn_beam_topk(R, BW, K, int(n_out), _ptr(beam_score), _ptr(logprob), _ptr(token),
+                                 _ptr(parent), _ptr(token_out), _ptr(score_out), _stream(stream)),
+           "xattn_beam_topk")
 
 
 def layer_step(dims, *, q, k_shared, v_shared, prefix_off, prefix_len, k_pool, v_pool, table_out,

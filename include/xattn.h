@@ -209,6 +209,31 @@ xattn_status xattn_cache_append(const xattn_dims* dims, const void* k_new, const
                                 int32_t* unshared_len, void* stream);
 
 /*
+ * Beam-search survivor selection for one decode step (xGR page, section 2.2
+ * xBeam: the Top-K sequences are chosen from the pool of every live beam's
+ * candidates; since a beam's candidates come sorted, a walk over the pool
+ * with a global min-heap stops a beam at its first candidate below the heap
+ * minimum). Per request r, the pool holds beam_width * top_k candidates
+ * (b, k) with score = beam_score[r][b] + logprob[r][b][k], added in float32.
+ * The n_out best by (score descending, pool index b * top_k + k ascending;
+ * -0.0 equals +0.0) are written in that order:
+ *   parent[r][i]    = b            (feeds xattn_cache_append's parent array)
+ *   token_out[r][i] = token[r][b][k]
+ *   score_out[r][i] = the score
+ * beam_score [R][beam_width] float32; logprob [R][beam_width][top_k]
+ * float32, every row non-increasing along k (required: the walk stops a
+ * beam early); scores finite or -inf (no NaN); token [R][beam_width][top_k]
+ * int32; outputs [R][n_out]. One workgroup per request, no workspace.
+ * XATTN_ERR_INVALID_ARG for null pointers or n_out > beam_width * top_k;
+ * XATTN_ERR_UNSUPPORTED if beam_width > 8192, n_out > 4096 or
+ * top_k > 8192 - n_out. n_out = 0 or num_requests = 0 enqueue nothing.
+ */
+xattn_status xattn_beam_topk(int32_t num_requests, int32_t beam_width, int32_t top_k,
+                             int32_t n_out, const float* beam_score, const float* logprob,
+                             const int32_t* token, int32_t* parent, int32_t* token_out,
+                             float* score_out, void* stream);
+
+/*
  * Multi-layer decode step as one HIP graph (xGR page, section 2.3 xSchedule:
  * device work is captured once into a static graph and submitted as a whole,
  * cutting kernel-launch overhead and CPU involvement; the xLLM page's engine

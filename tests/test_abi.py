@@ -160,3 +160,16 @@ def test_step_graph_argument_checks(L):
     assert not h.value
     assert L.xattn_step_graph_launch(None, None) == xattn.XATTN_ERR_INVALID_ARG
     assert L.xattn_step_graph_destroy(None) == xattn.XATTN_OK
+
+
+def test_beam_topk_argument_checks(L):
+    f = L.xattn_beam_topk
+    P = [FAKE] * 6
+    assert f(1, 4, 4, 17, *P, None) == xattn.XATTN_ERR_INVALID_ARG       # n_out > pool
+    assert f(-1, 4, 4, 4, *P, None) == xattn.XATTN_ERR_INVALID_ARG
+    assert f(1, 0, 4, 4, *P, None) == xattn.XATTN_ERR_INVALID_ARG
+    assert f(1, 4, 4, 4, None, *P[1:], None) == xattn.XATTN_ERR_INVALID_ARG
+    assert f(1, 9000, 4, 4, *P, None) == xattn.XATTN_ERR_UNSUPPORTED     # too many beams
+    assert f(1, 8000, 8000, 4096, *P, None) == xattn.XATTN_ERR_UNSUPPORTED
+    assert f(0, 4, 4, 4, *P, None) == xattn.XATTN_OK                     # nothing to do
+    assert f(1, 4, 4, 0, *P, None) == xattn.XATTN_OK
