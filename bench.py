@@ -1,8 +1,10 @@
 """Benchmark: staged beam-search decode attention on one MI355X.
 
-One step = one decode step of every layer: per layer, xattn_cache_append of
-the step's new tokens (token-granular K/V write and slot-table rewrite) and
-then xattn_decode, on n_layers distinct layer buffers (distinct Q, prompt KV,
+One step = one decode step: xattn_beam_topk picks each request's surviving
+beams from its beam_width x top_k candidate pool, then per layer
+xattn_cache_append of the step's new tokens (token-granular K/V write and
+slot-table rewrite, with the selected parents) and xattn_decode, on n_layers
+distinct layer buffers (distinct Q, prompt KV,
 Non-Shared pool, slot tables and lengths per layer, so the working set
 defeats the 256 MB Infinity Cache). By default the whole step is one
 captured HIP graph (xattn_step_graph_*), launched once per step; --eager
@@ -224,6 +226,14 @@ def main():
         o, lse, ws, nb = dv.alloc_outputs(d, 2)
         layers.append((d, o, lse, ws, nb, table_in, table_out, t_last))
     ulen0 = ulen_all.clone()
+    # The step opens with the survivor selection (beam width x top-k pool per
+    # request, top-k = beam width) whose parents every layer's append reads.
+    topk_k = max(1, min(w0.B, 512))
+    tx = inputs.make_topk("select", R=w0.R, BW=w0.B, K=topk_k, n_out=w0.B, seed_key=(700, 0))
+    sel_in = [torch.from_numpy(v).cuda() for v in (tx.beam_score, tx.logprob, tx.token)]
+    sel_parent = torch.empty((w0.R, w0.B), dtype=torch.int32, device="cuda")
+    sel_tok = torch.empty_like(sel_parent)
+    sel_score = torch.empty((w0.R, w0.B), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     plan = xattn.get_plan(layers[0][0].dims, 2)
     alg = algorithmic(w0)
@@ -235,9 +245,11 @@ def main():
 
     def eager_step(evs):
         ulen_all.copy_(ulen0)
+        xattn.beam_topk(*sel_in, w0.B, sel_parent, sel_tok, sel_score)
         for (d, o, lse, ws, nb, tin, tout, t_last), (e0, e1) in zip(layers, evs):
             if t_last is not None:
-                dv.append_step(d, t_last, table_in=tin, table_out=tout)
+                xattn.cache_append(d.dims, d.k_new[t_last], d.v_new[t_last], sel_parent, d.slot_base,
+                                   d.active[t_last], d.k_pool, d.v_pool, tin, tout, d.unshared_len)
             e0.record()
             xattn.decode(d.dims, d.q, d.k_shared, d.v_shared, d.prefix_off, d.prefix_len, d.k_pool,
                          d.v_pool, tout, d.unshared_len, o, lse, ws if nb else None, nb)
@@ -247,8 +259,15 @@ def main():
     warm_evs = new_events()
     if not args.eager:
         # The whole step (every layer's append and decode) as one graph.
-        step_graph = xattn.StepGraph([dv.layer_step(d, o, lse, ws, nb, tin, tout, t_last)
-                                      for (d, o, lse, ws, nb, tin, tout, t_last) in layers])
+        steps = []
+        for (d, o, lse, ws, nb, tin, tout, t_last) in layers:
+            st = dv.layer_step(d, o, lse, ws, nb, tin, tout, t_last)
+            st.parent = sel_parent.data_ptr()
+            steps.append(st)
+        select = xattn.beam_select(*sel_in, w0.B, sel_parent, sel_tok, sel_score)
+        step_graph = xattn.StepGraph(steps, select=select)
+        select_graph = xattn.StepGraph([], select=xattn.beam_select(*sel_in, w0.B, sel_parent, sel_tok,
+                                                                    sel_score))
         # Every layer's decode alone, back to back in one graph, to time the
         # decode kernel with HIP events around its launches (the runtime
         # PyTorch ships cannot record events inside a captured graph).
@@ -278,6 +297,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
+    select_us = None
     if args.eager:
         call_ms = np.array([[e0.elapsed_time(e1) for (e0, e1) in evs] for evs in step_evs])
         call_us = float(call_ms.mean() * 1e3)
@@ -293,10 +313,18 @@ def main():
             e0.record()
             decode_graph.launch()
             e1.record()
+        spairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(K)]
+        for e0, e1 in spairs:
+            e0.record()
+            select_graph.launch()
+            e1.record()
         torch.cuda.synchronize()
         call_us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in pairs]) * 1e3 / n_layers)
+        select_us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in spairs]) * 1e3)
         step_graph.close()
         decode_graph.close()
+        select_graph.close()
 
     ms_per_step = ms_total / K
     value = w0.N_b * n_layers / (ms_per_step / 1e3)
@@ -335,7 +363,9 @@ def main():
         "dtype": w0.dtype,
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[str(cfg)], "n_layers": n_layers,
-                   "beams_per_call": w0.N_b, "step": "append + decode per layer",
+                   "beams_per_call": w0.N_b,
+                   "step": "beam selection (%d x %d x %d pool -> %d beams per request), then "
+                           "append + decode per layer" % (w0.R, w0.B, topk_k, w0.B),
                    "launch": "eager" if args.eager else "graph", "plan": plan},
         "unique_kv_GBps": round(alg["unique_kv"] / call_s / 1e9, 1),
         "total_GBps": round(alg["total"] / call_s / 1e9, 1),
@@ -343,6 +373,7 @@ def main():
         "wall_s_timed": round(wall, 4),
         "step_GBps": round(n_layers * (alg["total"] + append_bytes(w0)) / (ms_per_step * 1e-3) / 1e9, 1),
         "roofline": roof,
+        "beam_select_us": None if select_us is None else round(select_us, 3),
     }
     if not args.no_cpu_baseline:
         print("timing the oracle on host cores ...", file=sys.stderr, flush=True)

@@ -1,6 +1,7 @@
-// Multi-layer decode step captured into one HIP graph: per layer the
-// Non-Shared append, then the fused decode, exactly as the eager entry points
-// enqueue them (they are called on a capture stream). Nothing in either path
+// Multi-layer decode step captured into one HIP graph: the optional beam
+// selection, then per layer the Non-Shared append and the fused decode,
+// exactly as the eager entry points enqueue them (they are called on a
+// capture stream). Nothing in either path
 // records a memset, so the graph replays cleanly; the split-merge counters in
 // each layer's workspace return to zero at the end of every launch.
 #include <hip/hip_runtime.h>
@@ -16,7 +17,14 @@ struct xattn_step_graph {
 
 namespace {
 
-xattn_status capture_layers(const xattn_layer_step* layers, int n, hipStream_t cs) {
+xattn_status capture_step(const xattn_beam_select* sel, const xattn_layer_step* layers, int n,
+                          hipStream_t cs) {
+  if (sel) {
+    const xattn_status e = xattn_beam_topk(sel->num_requests, sel->beam_width, sel->top_k, sel->n_out,
+                                           sel->beam_score, sel->logprob, sel->token, sel->parent,
+                                           sel->token_out, sel->score_out, cs);
+    if (e != XATTN_OK) return e;
+  }
   for (int i = 0; i < n; ++i) {
     const xattn_layer_step& l = layers[i];
     xattn_status e;
@@ -43,18 +51,20 @@ xattn_status capture_layers(const xattn_layer_step* layers, int n, hipStream_t c
 
 extern "C" {
 
-xattn_status xattn_step_graph_create(const xattn_layer_step* layers, int32_t n_layers,
+xattn_status xattn_step_graph_create(const xattn_beam_select* select,
+                                     const xattn_layer_step* layers, int32_t n_layers,
                                      xattn_step_graph** out) {
   if (!out) return XATTN_ERR_INVALID_ARG;
   *out = nullptr;
-  if (!layers || n_layers < 1) return XATTN_ERR_INVALID_ARG;
+  if (n_layers < 0 || (n_layers > 0 && !layers) || (n_layers == 0 && !select))
+    return XATTN_ERR_INVALID_ARG;
   hipStream_t cs = nullptr;
   if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return XATTN_ERR_HIP;
   if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
     hipStreamDestroy(cs);
     return XATTN_ERR_HIP;
   }
-  const xattn_status e = capture_layers(layers, n_layers, cs);
+  const xattn_status e = capture_step(select, layers, n_layers, cs);
   hipGraph_t graph = nullptr;
   const hipError_t ce = hipStreamEndCapture(cs, &graph);
   hipStreamDestroy(cs);

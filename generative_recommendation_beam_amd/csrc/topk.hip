@@ -7,9 +7,9 @@
 // order-preserving unsigned form on top, the complement of its pool index
 // below, so every key is distinct and "larger key" means "higher score, then
 // smaller index" - exactly the required order.
-//  1. Seed: the first (best) candidate of every beam. If there are at least
-//     n_out beams, the n_out-th largest seed key is a lower bound tau for the
-//     n_out-th largest key of the whole pool.
+//  1. Seed: the best few candidates of every beam (about 4 * n_out keys). If
+//     there are at least n_out of them, the n_out-th largest is a lower bound
+//     tau for the n_out-th largest key of the whole pool.
 //  2. Walk: beams are scanned in rounds of kChunk candidates; a beam takes
 //     part in the next round only while its last scanned candidate still
 //     reaches tau (early termination). Candidates with key >= tau are
@@ -72,12 +72,23 @@ __global__ __launch_bounds__(kThreads) void beam_topk_kernel(TopkArgs a) {
   const float* bs = a.beam_score + (int64_t)r * BW;
   const float* lp = a.logprob + (int64_t)r * BW * K;
 
-  // 1. Seed threshold.
+  // 1. Seed threshold from a sample: the best m candidates of every beam
+  //    (m chosen so the sample holds about 4 * n_out keys and fits in LDS).
+  //    Its n_out-th largest key bounds the pool's from below.
   uint64_t tau = 0;
-  if (BW >= N) {
-    const int n2 = next_pow2(BW);
-    for (int i = tid; i < n2; i += kThreads)
-      keys[i] = i < BW ? make_key(bs[i] + lp[(int64_t)i * K], (uint32_t)i * (uint32_t)K) : 0ull;
+  int m = (4 * N + BW - 1) / BW;
+  m = max(1, min(m, min(K, kTopkCap / BW)));
+  const int n_s = BW * m;
+  if (n_s >= N) {
+    const int n2 = next_pow2(n_s);
+    for (int i = tid; i < n2; i += kThreads) {
+      uint64_t key = 0ull;
+      if (i < n_s) {
+        const int b = i / m, k = i - (i / m) * m;
+        key = make_key(bs[b] + lp[(int64_t)b * K + k], (uint32_t)b * (uint32_t)K + (uint32_t)k);
+      }
+      keys[i] = key;
+    }
     __syncthreads();
     sort_desc(keys, n2);
     tau = keys[N - 1];

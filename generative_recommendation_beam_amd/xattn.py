@@ -61,6 +61,14 @@ class LayerStep(ctypes.Structure):
                 ("decode_end", P_)]
 
 
+class BeamSelect(ctypes.Structure):
+    """The survivor selection that opens a captured step (xattn_beam_select)."""
+    _fields_ = [("num_requests", ctypes.c_int32), ("beam_width", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("n_out", ctypes.c_int32), ("beam_score", P_),
+                ("logprob", P_), ("token", P_), ("parent", P_), ("token_out", P_),
+                ("score_out", P_)]
+
+
 class XattnError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -102,8 +110,8 @@ def lib():
     L.xattn_beam_topk.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   P, P, P, P, P, P, P]
     L.xattn_step_graph_create.restype = ctypes.c_int
-    L.xattn_step_graph_create.argtypes = [ctypes.POINTER(LayerStep), ctypes.c_int32,
-                                          ctypes.POINTER(ctypes.c_void_p)]
+    L.xattn_step_graph_create.argtypes = [ctypes.POINTER(BeamSelect), ctypes.POINTER(LayerStep),
+                                          ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
     L.xattn_step_graph_launch.restype = ctypes.c_int
     L.xattn_step_graph_launch.argtypes = [P, P]
     L.xattn_step_graph_destroy.restype = ctypes.c_int
@@ -230,14 +238,26 @@ def layer_step(dims, *, q, k_shared, v_shared, prefix_off, prefix_len, k_pool, v
     return st
 
 
+def beam_select(beam_score, logprob, token, n_out, parent, token_out, score_out) -> BeamSelect:
+    """Fill an xattn_beam_select from tensors (kept alive by the result)."""
+    R, BW, K = (int(x) for x in logprob.shape)
+    sel = BeamSelect(R, BW, K, int(n_out), _ptr(beam_score), _ptr(logprob), _ptr(token),
+                     _ptr(parent), _ptr(token_out), _ptr(score_out))
+    sel.keep_alive = [beam_score, logprob, token, parent, token_out, score_out]
+    return sel
+
+
 class StepGraph:
     """A captured multi-layer decode step (xattn_step_graph_*)."""
 
-    def __init__(self, steps):
-        self._steps = list(steps)  # their keep_alive lists pin the graph's buffers
-        arr = (LayerStep * len(steps))(*steps)
+    def __init__(self, steps, select=None):
+        # the LayerSteps' (and BeamSelect's) keep_alive lists pin the graph's buffers
+        self._steps = list(steps)
+        self._select = select
+        arr = (LayerStep * max(len(steps), 1))(*steps)
         h = ctypes.c_void_p(None)
-        _check(lib().xattn_step_graph_create(arr, len(steps), ctypes.byref(h)),
+        _check(lib().xattn_step_graph_create(ctypes.byref(select) if select is not None else None,
+                                             arr, len(steps), ctypes.byref(h)),
                "xattn_step_graph_create")
         self._h = h
 

@@ -242,12 +242,15 @@ xattn_status xattn_beam_topk(int32_t num_requests, int32_t beam_width, int32_t t
  * per-call host launch path costs more than the kernel itself.
  *
  * Each layer is self-contained: its own pool, slot tables and lengths. The
- * step runs, for every layer in order, xattn_cache_append (skipped when
- * k_new is NULL) and then xattn_decode on the table the append wrote
- * (table_out), with the arguments below exactly as those calls take them.
+ * step first runs the optional survivor selection (xattn_beam_select, the
+ * xattn_beam_topk arguments; its parent output is what the layers' appends
+ * normally read), then, for every layer in order, xattn_cache_append
+ * (skipped when k_new is NULL) and xattn_decode on the table the append
+ * wrote (table_out), with the arguments below exactly as those calls take
+ * them.
  * Positions are read from device memory when the graph runs, so one graph
- * serves every decode step: refill q / k_new / v_new / parent in place and
- * launch it again. If decode_begin / decode_end are not NULL (hipEvent_t
+ * serves every decode step: refill the candidates, q, k_new and v_new in
+ * place and launch it again. If decode_begin / decode_end are not NULL (hipEvent_t
  * created with timing enabled), they are captured as external event-record
  * nodes around the layer's decode, recorded on every launch; a HIP runtime
  * that cannot capture external event records (the one PyTorch 2.10 ships
@@ -278,16 +281,31 @@ typedef struct {
   void* decode_end;          /* hipEvent_t or NULL */
 } xattn_layer_step;
 
+typedef struct {
+  int32_t num_requests;
+  int32_t beam_width;
+  int32_t top_k;
+  int32_t n_out;
+  const float* beam_score;
+  const float* logprob;
+  const int32_t* token;
+  int32_t* parent;
+  int32_t* token_out;
+  float* score_out;
+} xattn_beam_select;
+
 typedef struct xattn_step_graph xattn_step_graph;  /* opaque */
 
 /*
- * Capture the step for n_layers >= 1 layers and instantiate it. Every
+ * Capture the step (select may be NULL: no selection) for n_layers >= 0
+ * layers (at least one of the two) and instantiate it. Every
  * argument is validated as the eager calls validate theirs; on any error
  * nothing is kept and *graph is left NULL. This call (and only this one, with
  * destroy) allocates: the graph, its executable form and a capture stream.
  * XATTN_ERR_HIP if capture or instantiation fails.
  */
-xattn_status xattn_step_graph_create(const xattn_layer_step* layers, int32_t n_layers,
+xattn_status xattn_step_graph_create(const xattn_beam_select* select,
+                                     const xattn_layer_step* layers, int32_t n_layers,
                                      xattn_step_graph** graph);
 /* Enqueue one step on `stream`. The graph's buffers must not be in use by
  * other work on other streams meanwhile. */

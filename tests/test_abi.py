@@ -153,10 +153,10 @@ def test_library_has_no_undefined_internal_symbols(L):
 def test_step_graph_argument_checks(L):
     """Rejected before any stream or graph is made (no GPU needed)."""
     h = ctypes.c_void_p(None)
-    assert L.xattn_step_graph_create(None, 1, ctypes.byref(h)) == xattn.XATTN_ERR_INVALID_ARG
+    assert L.xattn_step_graph_create(None, None, 1, ctypes.byref(h)) == xattn.XATTN_ERR_INVALID_ARG
     arr = (xattn.LayerStep * 1)()
-    assert L.xattn_step_graph_create(arr, 0, ctypes.byref(h)) == xattn.XATTN_ERR_INVALID_ARG
-    assert L.xattn_step_graph_create(arr, 1, None) == xattn.XATTN_ERR_INVALID_ARG
+    assert L.xattn_step_graph_create(None, arr, 0, ctypes.byref(h)) == xattn.XATTN_ERR_INVALID_ARG
+    assert L.xattn_step_graph_create(None, arr, 1, None) == xattn.XATTN_ERR_INVALID_ARG
     assert not h.value
     assert L.xattn_step_graph_launch(None, None) == xattn.XATTN_ERR_INVALID_ARG
     assert L.xattn_step_graph_destroy(None) == xattn.XATTN_OK
