@@ -43,10 +43,55 @@ __device__ __forceinline__ int next_pow2(int n) {
   return p;
 }
 
-// Sort keys[0, n) descending; n is a power of two. Whole workgroup.
+// Bitonic sort of keys[0, n) into descending order; n is a power of two,
+// at most kTopkCap. Whole workgroup. Element i lives in thread i % kThreads
+// (slot i / kThreads) while it is in registers, so every compare-exchange at
+// a stride below 64 pairs two lanes of one wavefront and runs on register
+// shuffles with no barrier; strides of 64 and more go through LDS.
+constexpr int kSortSlots = kTopkCap / kThreads;
+
+__device__ __forceinline__ void reg_steps(uint64_t* v, int n, int size, int smax) {
+  const int tid = threadIdx.x;
+  for (int stride = smax; stride >= 1; stride >>= 1) {
+#pragma unroll
+    for (int q = 0; q < kSortSlots; ++q) {
+      if (q * kThreads < n) {  // uniform
+        const int i = q * kThreads + tid;
+        const uint64_t p = __shfl_xor(v[q], stride);
+        const bool keep_max = ((i & size) == 0) == ((i & stride) == 0);
+        v[q] = keep_max ? (v[q] > p ? v[q] : p) : (v[q] < p ? v[q] : p);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void load_regs(uint64_t* v, const uint64_t* keys, int n) {
+#pragma unroll
+  for (int q = 0; q < kSortSlots; ++q) {
+    const int i = q * kThreads + threadIdx.x;
+    v[q] = i < n ? keys[i] : 0ull;
+  }
+}
+
+__device__ __forceinline__ void store_regs(const uint64_t* v, uint64_t* keys, int n) {
+#pragma unroll
+  for (int q = 0; q < kSortSlots; ++q) {
+    const int i = q * kThreads + threadIdx.x;
+    if (i < n) keys[i] = v[q];
+  }
+}
+
+// Caller: keys[0, n) written and visible (a barrier since). Ends with a
+// barrier, the sorted keys in LDS.
 __device__ void sort_desc(uint64_t* keys, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+  uint64_t v[kSortSlots];
+  load_regs(v, keys, n);
+  for (int size = 2; size <= n && size <= 64; size <<= 1) reg_steps(v, n, size, size >> 1);
+  __syncthreads();  // every load done before any store
+  store_regs(v, keys, n);
+  __syncthreads();
+  for (int size = 128; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride >= 64; stride >>= 1) {
       for (int t = threadIdx.x; t < (n >> 1); t += blockDim.x) {
         const int i = 2 * t - (t & (stride - 1));
         const int j = i + stride;
@@ -59,13 +104,18 @@ __device__ void sort_desc(uint64_t* keys, int n) {
       }
       __syncthreads();
     }
+    load_regs(v, keys, n);
+    reg_steps(v, n, size, 32);
+    __syncthreads();
+    store_regs(v, keys, n);
+    __syncthreads();
   }
 }
 
 __global__ __launch_bounds__(kThreads) void beam_topk_kernel(TopkArgs a) {
   __shared__ uint64_t keys[kTopkCap];
-  __shared__ uint8_t active[2][kTopkMaxBeams];
-  __shared__ int s_count, s_more;
+  __shared__ int act[2][kTopkMaxBeams];  // beams still walking, per round parity
+  __shared__ int s_count, s_nact[2];
   const int r = blockIdx.x;
   const int BW = a.BW, K = a.K, N = a.n_out;
   const int tid = threadIdx.x;
@@ -95,22 +145,28 @@ __global__ __launch_bounds__(kThreads) void beam_topk_kernel(TopkArgs a) {
     __syncthreads();
   }
 
-  // 2. Walk with early termination.
-  if (tid == 0) s_count = 0;
-  for (int b = tid; b < BW; b += kThreads) active[0][b] = 1;
+  // 2. Walk with early termination. Round 0 scans the first kChunk
+  //    candidates of every beam; each later round splits the workgroup's
+  //    kThreads * 4 candidate slots evenly over the beams still going (a
+  //    beam goes on while the last candidate it scanned reaches tau and
+  //    candidates remain), so a few strong beams finish in few rounds.
+  if (tid == 0) {
+    s_count = 0;
+    s_nact[0] = s_nact[1] = 0;
+  }
   __syncthreads();
   bool overflow = false;
   int n_found = 0;
-  constexpr int Q = kChunk / 4;  // quads of candidates per beam per round
-  for (int j = 0, cur = 0; j * kChunk < K; ++j, cur ^= 1) {
-    if (tid == 0) s_more = 0;
-    for (int b = tid; b < BW; b += kThreads) active[cur ^ 1][b] = 0;
-    __syncthreads();
-    for (int u = tid; u < BW * Q; u += kThreads) {
-      const int b = u / Q, q = u - b * Q;
-      if (!active[cur][b]) continue;
+  int n_act = BW;  // beams in this round (round 0: all, in order)
+  int pos = 0;     // first candidate of this round (the same for every beam)
+  for (int round = 0;; ++round) {
+    const int chunk = round == 0 ? kChunk : max(kChunk, ((kThreads * 4) / n_act) & ~3);
+    const int Q = chunk / 4;
+    for (int u = tid; u < n_act * Q; u += kThreads) {
+      const int ai = u / Q, q = u - ai * Q;
+      const int b = round == 0 ? ai : act[round & 1][ai];
       const float sb = bs[b];
-      const int k0 = j * kChunk + 4 * q;
+      const int k0 = pos + 4 * q;
       uint64_t kk[4];
       int nk = 0;
 #pragma unroll
@@ -123,32 +179,30 @@ __global__ __launch_bounds__(kThreads) void beam_topk_kernel(TopkArgs a) {
         }
       }
       if (nk > 0) {
-        const int pos = atomicAdd(&s_count, nk);
+        const int at = atomicAdd(&s_count, nk);
         int w = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (k0 + e < K && kk[e] >= tau) {
-            if (pos + w < kTopkCap) keys[pos + w] = kk[e];
+            if (at + w < kTopkCap) keys[at + w] = kk[e];
             ++w;
           }
         }
       }
-      // the beam goes on only if its last candidate of this round still
-      // reaches tau and candidates remain
-      if (q == Q - 1 && k0 + 3 < K - 1 && kk[3] >= tau) {
-        active[cur ^ 1][b] = 1;
-        s_more = 1;
-      }
+      if (q == Q - 1 && k0 + 3 < K - 1 && kk[3] >= tau)
+        act[(round + 1) & 1][atomicAdd(&s_nact[(round + 1) & 1], 1)] = b;
     }
     __syncthreads();
-    const int more = s_more;
+    n_act = s_nact[(round + 1) & 1];
     n_found = s_count;
-    __syncthreads();  // every thread has read both before thread 0 resets them
+    if (tid == 0) s_nact[round & 1] = 0;  // the counter the next round appends to
+    __syncthreads();
+    pos += chunk;
     if (n_found > kTopkCap) {
       overflow = true;
       break;
     }
-    if (!more) break;
+    if (n_act == 0) break;
   }
 
   int n_top;
