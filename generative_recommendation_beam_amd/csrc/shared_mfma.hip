@@ -393,9 +393,17 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   // address the prompt through descriptors bounded to its P_r rows, so keys
   // past the prompt read as zero (they are masked) and no load leaves it; the
   // only per-lane operand is the loop-invariant offset.
+  // Key groups (one workgroup per CU): the row tiles of a (request, kv
+  // head) walk the full super-tiles in rotated orders, each starting at its
+  // own, so their first loads fetch different parts of the prompt from HBM
+  // and every later load finds its super-tile already in L2, brought in by
+  // the workgroup that started there. The last (possibly partial) super-tile
+  // stays last. The softmax result does not depend on the order.
+  const int rot = (KG == 2 && nsup > 2) ? tile % (nsup - 1) : 0;
   auto issue_tile = [&](int t) {
     lds_char* buf = lsm + (t % NS) * SBUF + wave * 1024;
-    const uint32_t tile_bytes = (uint32_t)((kbeg + t * ST) * TG::ROWB);
+    const int pt = t < nsup - 1 ? (t + rot) % (nsup - 1) : t;  // super-tile loaded at step t
+    const uint32_t tile_bytes = (uint32_t)((kbeg + pt * ST) * TG::ROWB);
 #pragma unroll
     for (int j = 0; j < LP::NJ; ++j) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, buf + LP::lds_off(j), 16, lp.k[j], tile_bytes, 0, 0);
@@ -422,28 +430,47 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   // Non-Shared tokens: in the generated-token member, or (no such member) in
   // prompt split 0. They are folded in after the prompt tiles. With one
   // workgroup per CU (registers to spare, nothing else to hide latency
-  // behind) the slots and the first NPF tokens are fetched before the tile
-  // loop; otherwise everything is fetched after it while the CU's other
-  // workgroup computes.
+  // behind) the length and the first NPF tokens' slot cells are read with
+  // the query rows, and those tokens' K/V rows are requested right after the
+  // first super-tile's compute, so that none of this chain holds up the
+  // tiles; otherwise everything is fetched after the loop while the CU's
+  // other workgroup computes.
   const bool do_ns = a.k_pool != nullptr && (gen_only || (!a.gen_member && member == 0));
   constexpr int NPF = (NS * SBUF > 80 * 1024 && NW <= 4) ? 2 : 0;
   NonShared<D, KG> ns;
   ns.L = 0;
   ns.kg = kg;
-  if (do_ns) ns.init(a, r, h, bq, kg, hh);
-  // The prefetch below is branch-free (a branch would make the compiler wait
-  // for the prompt tiles before these loads): missing tokens re-read the
-  // last one, and without Non-Shared tokens every read goes to the first
-  // query row, which always exists.
   int pslot[NPF > 0 ? NPF : 1];
   uint4 pk[NPF > 0 ? NPF : 1][NDC];
   uint2 pv[NPF > 0 ? NPF : 1][NDB][4];
   if (NPF > 0) {
-    const int32_t* trow = ns.L > 0 ? ns.trow : a.prefix_len;
-    const int smask = ns.L > 0 ? -1 : 0;
+    // Branch-free (a branch here would make the compiler wait for these
+    // reads where the paths join): without Non-Shared tokens the reads go
+    // to prefix_len[0], which always exists; slot cells are clamped to the
+    // row and masked to slot 0 once the length is known.
+    const int32_t* lenp = do_ns ? a.unshared_len + r : a.prefix_len;
+    const int32_t* trow = do_ns ? a.slot_table + ((int64_t)r * s.B + bq) * s.T_max : a.prefix_len;
+    const int tlast = do_ns ? s.T_max - 1 : 0;
+    const int len = *lenp;
 #pragma unroll
-    for (int u = 0; u < NPF; ++u) pslot[u] = trow[max(min(kg + KG * u, ns.L - 1), 0)] & smask;
+    for (int u = 0; u < NPF; ++u) pslot[u] = trow[min(kg + KG * u, tlast)];
+    ns.L = do_ns ? __builtin_amdgcn_readfirstlane(len) : 0;
+    ns.hkv = s.Hkv;
+    ns.kp = do_ns ? a.k_pool + (int64_t)h * D + 8 * hh : a.q;
+    ns.vp = do_ns ? a.v_pool + (int64_t)h * D + 4 * hh : a.q;
+    ns.trow = trow;
+  } else if (do_ns) {
+    ns.init(a, r, h, bq, kg, hh);
   }
+  // K/V rows of the first NPF tokens (missing ones read slot 0 / the first
+  // query row, in bounds either way).
+  auto fetch_tokens = [&]() {
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) {
+      const int sl = ns.has(u) ? pslot[u] : 0;
+      ns.fetch(sl, pk[u], pv[u]);
+    }
+  };
 
   // Super-tiles 0 .. NS-2 go in flight next.
   int issued = 0;
@@ -455,12 +482,6 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
     }
   }
 
-  if (NPF > 0) {
-    NonShared<D, KG> pf = ns;
-    if (ns.L == 0) pf.kp = pf.vp = a.q;
-#pragma unroll
-    for (int u = 0; u < NPF; ++u) pf.fetch(pslot[u], pk[u], pv[u]);
-  }
 
   f32x16_t oacc[NDB];
 #pragma unroll
@@ -493,7 +514,10 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
 
   // Wait for super-tile `it`, then refill the buffer super-tile it-1 used.
   auto advance = [&](int it) {
-    wait_tiles<LPT>(min(issued - 1 - it, NS - 2));
+    if (NPF > 0 && NS == 2 && it == 1)  // the token rows requested after tile 1's loads may stay in flight
+      __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(NPF * (NDC + 4 * NDB)) : "memory");
+    else
+      wait_tiles<LPT>(min(issued - 1 - it, NS - 2));
     __syncthreads();  // super-tile `it` landed for every wave; it-1's buffer is free
     if (issued < nsup) {
       issue_tile(issued);
@@ -505,7 +529,12 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
     advance(it);
     tile_step<D, false>(smem + (it % NS) * SBUF + kg * TG::BUFB, kbase, vbase, qf, oacc, m_run, l_part, c,
                         hh, BN);
+    if (NPF > 0 && it == 0) {
+      __asm__ volatile("" ::: "memory");  // keep these loads after tile 1's
+      fetch_tokens();
+    }
   }
+  if (NPF > 0 && nsup <= 1) fetch_tokens();
   if (nsup > 0) {  // the last super-tile: this wave's tile may be partial or empty
     const int it = nsup - 1;
     advance(it);
