@@ -118,6 +118,52 @@ def cpu_baseline(layers_np, min_seconds=10.0):
                        f"of the same workload (fp64 numpy oracle, {used} worker processes, {el:.1f} s)")
 
 
+def paged_baseline(layers, K, xattn_call_us, xattn_step_ms):
+    """The same layers in a PagedAttention-style block-paged cache: per layer,
+    the copies branching beams make of their partial tail blocks, then the
+    per-beam paged decode. HIP events around every call, K rounds, queued
+    behind each other (each call outlasts its host launch)."""
+    import numpy as np
+    import torch
+    from generative_recommendation_beam_amd import device as dv
+    from generative_recommendation_beam_amd import xattn
+    paged = []
+    for (d, o, lse, ws, nb, tin, tout, t_last) in layers:
+        pc = dv.build_paged(d, tout)
+        pnb = xattn.paged_workspace_size(d.dims, pc.max_seq_len)
+        pws = torch.zeros(max(pnb, 1), dtype=torch.uint8, device="cuda")
+        paged.append((d, pc, o, lse, pws, pnb))
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    rounds = [[(ev(), ev(), ev()) for _ in paged] for _ in range(K)]
+    for d, pc, o, lse, pws, pnb in paged:  # warm-up
+        xattn.paged_copy_blocks(d.dims, pc.k_cache, pc.v_cache, pc.parent_tail, pc.spare)
+        dv.paged_decode(d, pc, o, lse, pws, pnb)
+    torch.cuda.synchronize()
+    start, end = ev(), ev()
+    start.record()
+    for r in rounds:
+        for (d, pc, o, lse, pws, pnb), (e0, e1, e2) in zip(paged, r):
+            e0.record()
+            xattn.paged_copy_blocks(d.dims, pc.k_cache, pc.v_cache, pc.parent_tail, pc.spare)
+            e1.record()
+            dv.paged_decode(d, pc, o, lse, pws, pnb)
+            e2.record()
+    end.record()
+    torch.cuda.synchronize()
+    copy_us = float(np.mean([[e0.elapsed_time(e1) for e0, e1, e2 in r] for r in rounds]) * 1e3)
+    dec_us = float(np.mean([[e1.elapsed_time(e2) for e0, e1, e2 in r] for r in rounds]) * 1e3)
+    step_ms = start.elapsed_time(end) / K
+    pc0 = paged[0][1]
+    return dict(decode_us_per_call=round(dec_us, 2), block_copy_us_per_call=round(copy_us, 2),
+                step_ms=round(step_ms, 4), blocks_per_layer=int(pc0.k_cache.shape[0]),
+                decode_speedup_xattn=round(dec_us / xattn_call_us, 2),
+                step_speedup_xattn=round(step_ms / xattn_step_ms, 2),
+                note="same layers, same attention; PagedAttention-style per-beam paged decode "
+                     "(16-token blocks, prompt blocks shared and re-read by every beam) plus the "
+                     "copy each beam makes of its parent's tail block; eager launches")
+
+
 def append_bytes(w):
     """Algorithmic bytes of one layer's append of the last step's tokens."""
     e = w.elem_bytes
@@ -185,6 +231,8 @@ def main():
     ap.add_argument("--rows-per-block", type=int, default=0, help="override rows per workgroup (0 = auto)")
     ap.add_argument("--stages", type=int, default=0, help="override LDS pipeline stages (0 = auto)")
     ap.add_argument("--key-groups", type=int, default=0, help="override key groups per workgroup (0 = auto)")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the PagedAttention-style baseline measured beside the step")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from the host instead of one captured step graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -375,6 +423,9 @@ def main():
         "roofline": roof,
         "beam_select_us": None if select_us is None else round(select_us, 3),
     }
+    if not args.no_paged and w0.dtype == "bf16":
+        print("timing the PagedAttention-style baseline ...", file=sys.stderr, flush=True)
+        result["paged_baseline"] = paged_baseline(layers, K, call_us, ms_per_step)
     if not args.no_cpu_baseline:
         print("timing the oracle on host cores ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(layers_np, args.cpu_seconds)

@@ -486,6 +486,77 @@ xattn_status xattn_cache_append(const xattn_dims* d, const void* k_new, const vo
   return hip_status(launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
+static size_t paged_ws_bytes(const xattn_dims* d, int32_t max_seq_len) {
+  const int nparts = max_seq_len > kPagedPart ? (max_seq_len + kPagedPart - 1) / kPagedPart : 1;
+  if (nparts <= 1) return 0;
+  const int64_t rows = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
+  return align256((size_t)nparts * rows * d->head_dim * sizeof(float)) +
+         align256((size_t)nparts * rows * sizeof(float));
+}
+
+static xattn_status paged_check(const xattn_dims* d, int32_t max_seq_len) {
+  xattn_status e = check_dims(d);
+  if (e != XATTN_OK) return e;
+  if (max_seq_len < 0) return XATTN_ERR_INVALID_ARG;
+  if (d->dtype != XATTN_BF16) return XATTN_ERR_UNSUPPORTED;
+  return XATTN_OK;
+}
+
+xattn_status xattn_paged_workspace_size(const xattn_dims* d, int32_t max_seq_len, size_t* bytes) {
+  xattn_status e = paged_check(d, max_seq_len);
+  if (e != XATTN_OK) return e;
+  if (!bytes) return XATTN_ERR_INVALID_ARG;
+  *bytes = paged_ws_bytes(d, max_seq_len);
+  return XATTN_OK;
+}
+
+xattn_status xattn_paged_decode(const xattn_dims* d, int32_t max_seq_len, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* seq_len, float* o, float* lse, void* ws, size_t ws_bytes,
+                                void* stream) {
+  xattn_status e = paged_check(d, max_seq_len);
+  if (e != XATTN_OK) return e;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_len || !o) return XATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return XATTN_ERR_INVALID_ARG;
+  if (max_blocks < 0 || (int64_t)max_blocks * kPagedBlock < max_seq_len) return XATTN_ERR_INVALID_ARG;
+  const size_t need = paged_ws_bytes(d, max_seq_len);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return XATTN_ERR_WORKSPACE;
+  PagedArgs a;
+  a.Hq = d->num_q_heads;
+  a.Hkv = d->num_kv_heads;
+  a.D = d->head_dim;
+  a.max_blocks = max_blocks;
+  a.nparts = max_seq_len > kPagedPart ? (max_seq_len + kPagedPart - 1) / kPagedPart : 1;
+  a.rows = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
+  a.scale_log2 = d->scale * 1.4426950408889634f;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.block_table = block_table;
+  a.seq_len = seq_len;
+  a.o = o;
+  a.lse = lse;
+  char* base = static_cast<char*>(ws);
+  a.part_o = need ? reinterpret_cast<float*>(base) : nullptr;
+  a.part_lse = need ? reinterpret_cast<float*>(base + align256((size_t)a.nparts * a.rows * a.D * sizeof(float)))
+                    : nullptr;
+  return hip_status(launch_paged_attn(a, static_cast<hipStream_t>(stream)));
+}
+
+xattn_status xattn_paged_copy_blocks(const xattn_dims* d, void* k_cache, void* v_cache, const int32_t* src,
+                                     const int32_t* dst, int32_t n, void* stream) {
+  xattn_status e = paged_check(d, 0);
+  if (e != XATTN_OK) return e;
+  if (n < 0) return XATTN_ERR_INVALID_ARG;
+  if (n == 0) return XATTN_OK;
+  if (!k_cache || !v_cache || !src || !dst || !aligned16(k_cache) || !aligned16(v_cache))
+    return XATTN_ERR_INVALID_ARG;
+  const int64_t block_elems = (int64_t)d->num_kv_heads * kPagedBlock * d->head_dim;
+  return hip_status(launch_copy_blocks(static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), src,
+                                       dst, n, block_elems, static_cast<hipStream_t>(stream)));
+}
+
 xattn_status xattn_beam_topk(int32_t num_requests, int32_t beam_width, int32_t top_k, int32_t n_out,
                              const float* beam_score, const float* logprob, const int32_t* token,
                              int32_t* parent, int32_t* token_out, float* score_out, void* stream) {

@@ -121,4 +121,25 @@ struct TopkArgs {
 };
 hipError_t launch_beam_topk(const TopkArgs& a, hipStream_t st);
 
+// ---- PagedAttention-style baseline (paged_attn.hip) ----
+constexpr int kPagedBlock = 16;   // tokens per cache block
+constexpr int kPagedPart = 512;   // tokens per partition of one beam's sequence
+struct PagedArgs {
+  int Hq, Hkv, D, max_blocks, nparts;
+  int64_t rows;                   // N_b * H_q
+  float scale_log2;
+  const uint16_t* q;              // [N_b][H_q][D] bf16
+  const uint16_t* k_cache;        // [num_blocks][H_kv][kPagedBlock][D]
+  const uint16_t* v_cache;
+  const int32_t* block_table;     // [N_b][max_blocks]
+  const int32_t* seq_len;         // [N_b]
+  float* o;                       // [N_b][H_q][D]
+  float* lse;                     // [N_b][H_q] or null
+  float* part_o;                  // [nparts][rows][D] when nparts > 1
+  float* part_lse;                // [nparts][rows]
+};
+hipError_t launch_paged_attn(const PagedArgs& a, hipStream_t st);
+hipError_t launch_copy_blocks(uint16_t* kc, uint16_t* vc, const int32_t* src, const int32_t* dst, int n,
+                              int64_t block_elems, hipStream_t st);
+
 }  // namespace xattn

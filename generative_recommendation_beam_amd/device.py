@@ -141,3 +141,109 @@ def layer_step(d: DeviceWorkload, o, lse, ws, nbytes, table_in, table_out, t_las
                             workspace_bytes=nbytes, decode_begin=decode_begin,
                             decode_end=decode_end, **app)
 
+
+
+# ---- PagedAttention-style comparison layout ----
+PAGED_BLOCK = 16
+
+
+@dataclass
+class PagedCache:
+    """The same caches as a DeviceWorkload, laid out the PagedAttention way:
+    16-token blocks [num_blocks][H_kv][16][D]; a request's full prompt blocks
+    are shared by its beams, and each beam owns blocks holding the prompt's
+    last partial block followed by its own generated tokens. `tail_block[n]`
+    is beam n's last block, `spare` one spare block per beam (the copy a
+    branching beam makes lands there)."""
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    block_table: torch.Tensor
+    seq_len: torch.Tensor
+    max_seq_len: int
+    tail_block: torch.Tensor
+    parent_tail: torch.Tensor
+    spare: torch.Tensor
+
+
+def build_paged(d: DeviceWorkload, table=None) -> PagedCache:
+    """Build the paged layout from d's prompt KV and (already built) Non-Shared
+    cache, reading generated tokens through `table` (default d.table). Data
+    preparation for the baseline: index arithmetic on the host, gathers on
+    the device."""
+    w = d.w
+    BS = PAGED_BLOCK
+    P = w.prefix_len.astype(np.int64)
+    L = w.unshared_len.astype(np.int64)
+    table = (d.table if table is None else table).cpu().numpy()
+    n_blocks = 0
+    shared = []
+    for r in range(w.R):
+        shared.append(list(range(n_blocks, n_blocks + int(P[r] // BS))))
+        n_blocks += int(P[r] // BS)
+    rows, seq = [], []
+    src_prompt, src_slot = [], []   # per cache token: prompt token index (h-free) or pool slot
+    priv_first = []
+    for r in range(w.R):
+        tail = int(P[r] % BS)
+        for b in range(w.B):
+            n = r * w.B + b
+            ntok = tail + int(L[r])
+            nb = (ntok + BS - 1) // BS
+            priv = list(range(n_blocks, n_blocks + nb))
+            n_blocks += nb
+            priv_first.append(priv)
+            rows.append(shared[r] + priv)
+            seq.append(int(P[r] + L[r]))
+    max_blocks = max([len(x) for x in rows] + [1])
+    bt = np.zeros((w.N_b, max_blocks), np.int32)
+    for n, row in enumerate(rows):
+        bt[n, :len(row)] = row
+    spare0 = n_blocks
+    total_blocks = n_blocks + w.N_b
+    # token map: for every (block, i) which source fills it
+    kind = np.zeros((total_blocks, BS), np.int8)       # 0 none, 1 prompt, 2 pool
+    idx = np.zeros((total_blocks, BS), np.int64)
+    for r in range(w.R):
+        off = int(w.prefix_off[r])
+        for j, blk in enumerate(shared[r]):
+            kind[blk] = 1
+            idx[blk] = off + j * BS + np.arange(BS)
+        tail = int(P[r] % BS)
+        for b in range(w.B):
+            n = r * w.B + b
+            toks = [(1, off + int(P[r]) - tail + i) for i in range(tail)]
+            toks += [(2, int(table[n, t])) for t in range(int(L[r]))]
+            for k, (kd, ix) in enumerate(toks):
+                blk = priv_first[n][k // BS]
+                kind[blk, k % BS] = kd
+                idx[blk, k % BS] = ix
+    dev = d.q.device
+    tdt = d.k_shared.dtype
+    kc = torch.zeros((total_blocks, w.Hkv, BS, w.D), dtype=tdt, device=dev)
+    vc = torch.zeros_like(kc)
+    kind_t = torch.from_numpy(kind).to(dev)
+    idx_t = torch.from_numpy(idx).to(dev)
+    for h in range(w.Hkv):
+        m1 = kind_t == 1
+        if bool(m1.any()):
+            kc[:, h][m1] = d.k_shared[h][idx_t[m1]]
+            vc[:, h][m1] = d.v_shared[h][idx_t[m1]]
+        m2 = kind_t == 2
+        if bool(m2.any()):
+            kc[:, h][m2] = d.k_pool[idx_t[m2], h]
+            vc[:, h][m2] = d.v_pool[idx_t[m2], h]
+    tail_block = np.array([row[-1] if row else 0 for row in rows], np.int32)
+    # the block a beam's tail was copied from at the last step: its parent's
+    t_last = w.T_steps - 1
+    parent = np.arange(w.N_b) if t_last < 1 else \
+        (np.arange(w.N_b) // w.B) * w.B + w.parents[t_last]
+    return PagedCache(k_cache=kc, v_cache=vc, block_table=torch.from_numpy(bt).to(dev),
+                      seq_len=torch.tensor(seq, dtype=torch.int32, device=dev), max_seq_len=max(seq + [0]),
+                      tail_block=torch.from_numpy(tail_block).to(dev),
+                      parent_tail=torch.from_numpy(tail_block[parent].astype(np.int32)).to(dev),
+                      spare=torch.arange(spare0, spare0 + w.N_b, dtype=torch.int32, device=dev))
+
+
+def paged_decode(d: DeviceWorkload, pc: PagedCache, o, lse, ws=None, nbytes=0, stream=None):
+    xattn.paged_decode(d.dims, pc.max_seq_len, d.q, pc.k_cache, pc.v_cache, pc.block_table, pc.seq_len, o,
+                       lse, ws if nbytes else None, nbytes, stream=stream)

@@ -21,6 +21,7 @@ XATTN_F32, XATTN_BF16 = 0, 1
 
 EXPORTED = ("xattn_workspace_size", "xattn_get_plan", "xattn_shared_stage", "xattn_unshared_stage",
             "xattn_merge", "xattn_decode", "xattn_cache_append", "xattn_beam_topk",
+            "xattn_paged_workspace_size", "xattn_paged_decode", "xattn_paged_copy_blocks",
             "xattn_step_graph_create",
             "xattn_step_graph_launch", "xattn_step_graph_destroy", "xattn_status_string")
 
@@ -106,6 +107,13 @@ def lib():
     L.xattn_decode.argtypes = [pd, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     L.xattn_cache_append.restype = ctypes.c_int
     L.xattn_cache_append.argtypes = [pd, P, P, P, P, P, P, P, P, P, P, P]
+    L.xattn_paged_workspace_size.restype = ctypes.c_int
+    L.xattn_paged_workspace_size.argtypes = [pd, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+    L.xattn_paged_decode.restype = ctypes.c_int
+    L.xattn_paged_decode.argtypes = [pd, ctypes.c_int32, P, P, P, P, ctypes.c_int32, P, P, P, P,
+                                     ctypes.c_size_t, P]
+    L.xattn_paged_copy_blocks.restype = ctypes.c_int
+    L.xattn_paged_copy_blocks.argtypes = [pd, P, P, P, P, ctypes.c_int32, P]
     L.xattn_beam_topk.restype = ctypes.c_int
     L.xattn_beam_topk.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   P, P, P, P, P, P, P]
@@ -205,6 +213,28 @@ def cache_append(dims, k_new, v_new, parent, slot_base, active, k_pool, v_pool, 
                                     _ptr(table_in), _ptr(table_out), _ptr(unshared_len),
                                     _stream(stream)),
            "xattn_cache_append")
+
+
+def paged_workspace_size(dims, max_seq_len) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().xattn_paged_workspace_size(ctypes.byref(dims), int(max_seq_len), ctypes.byref(n)),
+           "xattn_paged_workspace_size")
+    return int(n.value)
+
+
+def paged_decode(dims, max_seq_len, q, k_cache, v_cache, block_table, seq_len, o, lse=None,
+                 workspace=None, workspace_bytes=0, stream=None):
+    _check(lib().xattn_paged_decode(ctypes.byref(dims), int(max_seq_len), _ptr(q), _ptr(k_cache),
+                                    _ptr(v_cache), _ptr(block_table), int(block_table.shape[1]),
+                                    _ptr(seq_len), _ptr(o), _ptr(lse), _ptr(workspace),
+                                    int(workspace_bytes), _stream(stream)),
+           "xattn_paged_decode")
+
+
+def paged_copy_blocks(dims, k_cache, v_cache, src, dst, stream=None):
+    _check(lib().xattn_paged_copy_blocks(ctypes.byref(dims), _ptr(k_cache), _ptr(v_cache), _ptr(src),
+                                         _ptr(dst), int(src.shape[0]), _stream(stream)),
+           "xattn_paged_copy_blocks")
 
 
 def beam_topk(beam_score, logprob, token, n_out, parent, token_out, score_out, stream=None):

@@ -234,6 +234,37 @@ xattn_status xattn_beam_topk(int32_t num_requests, int32_t beam_width, int32_t t
                              float* score_out, void* stream);
 
 /*
+ * COMPARISON BASELINE: PagedAttention-style per-beam decode attention (xGR
+ * page, section 1: serving systems in the PagedAttention mould treat each
+ * beam as an independent sequence, so the shared prompt is loaded again for
+ * every beam and branching beams copy their partially filled blocks). It
+ * computes the same o / lse as xattn_decode for a beam whose sequence is its
+ * prompt followed by its own generated tokens, but from a block-paged cache:
+ *   k_cache, v_cache  [num_blocks][H_kv][16][D] bf16 (16-token blocks)
+ *   block_table       [N_b][max_blocks] int32: beam n's i-th block
+ *   seq_len           [N_b] int32, <= max_seq_len <= 16 * max_blocks
+ * Uses dims.num_requests, beam_width, num_q_heads, num_kv_heads, head_dim,
+ * scale; dtype must be XATTN_BF16 (else XATTN_ERR_UNSUPPORTED). Sequences
+ * longer than 512 tokens are split in partitions merged in a second launch;
+ * that needs xattn_paged_workspace_size bytes of workspace (0 otherwise).
+ */
+xattn_status xattn_paged_workspace_size(const xattn_dims* dims, int32_t max_seq_len, size_t* bytes);
+xattn_status xattn_paged_decode(const xattn_dims* dims, int32_t max_seq_len, const void* q,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* seq_len, float* o, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream);
+/*
+ * COMPARISON BASELINE: copy whole cache blocks (every kv head) src[i] ->
+ * dst[i], i < n, in both k_cache and v_cache ([num_blocks][H_kv][16][D]
+ * bf16): the copy-on-write a branching beam needs in a block-paged cache.
+ * Destination blocks must be distinct and not sources.
+ */
+xattn_status xattn_paged_copy_blocks(const xattn_dims* dims, void* k_cache, void* v_cache,
+                                     const int32_t* src, const int32_t* dst, int32_t n,
+                                     void* stream);
+
+/*
  * Multi-layer decode step as one HIP graph (xGR page, section 2.3 xSchedule:
  * device work is captured once into a static graph and submitted as a whole,
  * cutting kernel-launch overhead and CPU involvement; the xLLM page's engine
