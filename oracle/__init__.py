@@ -13,6 +13,8 @@ Modules:
   append     reference semantics of the token-granular cache update.
   beam_topk  reference semantics of beam-search survivor selection (the n_out
              best candidates by score, index tie-break).
+  cht        Feather's batch-forming structure by brute force (missing
+             counts from direct token comparison).
   pool       process-pool driver used to time the oracle on many cores.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against brute force,
