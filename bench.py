@@ -164,6 +164,45 @@ def paged_baseline(layers, K, xattn_call_us, xattn_step_ms):
                      "copy each beam makes of its parent's tail block; eager launches")
 
 
+def batch_former_timing():
+    """Host batch former (xattn_cht_*) on the Feather page's sensitivity
+    shape: 800 requests in 8 shuffled prefix groups, 1024-token prefixes plus
+    128 unique tokens, 16-token blocks; batches of up to 100 formed and
+    retired until none wait."""
+    import random
+    from generative_recommendation_beam_amd import xattn
+    rng = random.Random(11)
+    bs = 16
+    groups = [[rng.randint(0, 30000) for _ in range(1024)] for _ in range(8)]
+    order = [g for g in range(8) for _ in range(100)]
+    rng.shuffle(order)
+    reqs = [groups[g] + [rng.randint(0, 30000) for _ in range(128)] for g in order]
+    c = xattn.Cht(bs)
+    t0 = time.perf_counter()
+    for rid, toks in enumerate(reqs):
+        c.insert(rid, toks)
+    t1 = time.perf_counter()
+    batches, homogeneous = 0, 0
+    t_form = 0.0
+    while True:
+        s0 = time.perf_counter()
+        b = c.form_batch(100, 128 // bs)
+        t_form += time.perf_counter() - s0
+        if not b:
+            break
+        batches += 1
+        homogeneous += len({order[r] for r in b}) == 1
+        s0 = time.perf_counter()
+        for r in b:
+            c.complete(r)
+        t_form += time.perf_counter() - s0
+    c.close()
+    return dict(requests=len(reqs), insert_us_per_request=round((t1 - t0) / len(reqs) * 1e6, 2),
+                form_and_retire_us_per_request=round(t_form / len(reqs) * 1e6, 2), batches=batches,
+                homogeneous_batches=homogeneous,
+                note="host C++ through ctypes (the per-call Python overhead included)")
+
+
 def append_bytes(w):
     """Algorithmic bytes of one layer's append of the last step's tokens."""
     e = w.elem_bytes
@@ -426,6 +465,7 @@ def main():
     if not args.no_paged and w0.dtype == "bf16":
         print("timing the PagedAttention-style baseline ...", file=sys.stderr, flush=True)
         result["paged_baseline"] = paged_baseline(layers, K, call_us, ms_per_step)
+    result["batch_former"] = batch_former_timing()
     if not args.no_cpu_baseline:
         print("timing the oracle on host cores ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(layers_np, args.cpu_seconds)

@@ -22,7 +22,8 @@ XATTN_F32, XATTN_BF16 = 0, 1
 EXPORTED = ("xattn_workspace_size", "xattn_get_plan", "xattn_shared_stage", "xattn_unshared_stage",
             "xattn_merge", "xattn_decode", "xattn_cache_append", "xattn_beam_topk",
             "xattn_paged_workspace_size", "xattn_paged_decode", "xattn_paged_copy_blocks",
-            "xattn_step_graph_create",
+            "xattn_cht_create", "xattn_cht_destroy", "xattn_cht_insert", "xattn_cht_best",
+            "xattn_cht_admit", "xattn_cht_complete", "xattn_cht_form_batch", "xattn_step_graph_create",
             "xattn_step_graph_launch", "xattn_step_graph_destroy", "xattn_status_string")
 
 
@@ -114,6 +115,21 @@ def lib():
                                      ctypes.c_size_t, P]
     L.xattn_paged_copy_blocks.restype = ctypes.c_int
     L.xattn_paged_copy_blocks.argtypes = [pd, P, P, P, P, ctypes.c_int32, P]
+    i64 = ctypes.c_int64
+    L.xattn_cht_create.restype = ctypes.c_int
+    L.xattn_cht_create.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
+    L.xattn_cht_destroy.restype = ctypes.c_int
+    L.xattn_cht_destroy.argtypes = [P]
+    L.xattn_cht_insert.restype = ctypes.c_int
+    L.xattn_cht_insert.argtypes = [P, i64, P, i64]
+    L.xattn_cht_best.restype = ctypes.c_int
+    L.xattn_cht_best.argtypes = [P, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.xattn_cht_admit.restype = ctypes.c_int
+    L.xattn_cht_admit.argtypes = [P, i64]
+    L.xattn_cht_complete.restype = ctypes.c_int
+    L.xattn_cht_complete.argtypes = [P, i64]
+    L.xattn_cht_form_batch.restype = ctypes.c_int
+    L.xattn_cht_form_batch.argtypes = [P, ctypes.c_int32, i64, P, ctypes.POINTER(ctypes.c_int32)]
     L.xattn_beam_topk.restype = ctypes.c_int
     L.xattn_beam_topk.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   P, P, P, P, P, P, P]
@@ -235,6 +251,50 @@ def paged_copy_blocks(dims, k_cache, v_cache, src, dst, stream=None):
     _check(lib().xattn_paged_copy_blocks(ctypes.byref(dims), _ptr(k_cache), _ptr(v_cache), _ptr(src),
                                          _ptr(dst), int(src.shape[0]), _stream(stream)),
            "xattn_paged_copy_blocks")
+
+
+class Cht:
+    """Host-side batch former (xattn_cht_*): cumulative block hashes, a
+    working set of the active batch and a min-heap by missing blocks."""
+
+    def __init__(self, block_size: int):
+        h = ctypes.c_void_p(None)
+        _check(lib().xattn_cht_create(int(block_size), ctypes.byref(h)), "xattn_cht_create")
+        self._h = h
+
+    def insert(self, rid: int, tokens) -> None:
+        arr = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        _check(lib().xattn_cht_insert(self._h, int(rid), arr.ctypes.data if arr.size else None,
+                                      int(arr.size)), "xattn_cht_insert")
+
+    def best(self):
+        rid, miss = ctypes.c_int64(0), ctypes.c_int64(0)
+        _check(lib().xattn_cht_best(self._h, ctypes.byref(rid), ctypes.byref(miss)), "xattn_cht_best")
+        return int(rid.value), int(miss.value)
+
+    def admit(self, rid: int) -> None:
+        _check(lib().xattn_cht_admit(self._h, int(rid)), "xattn_cht_admit")
+
+    def complete(self, rid: int) -> None:
+        _check(lib().xattn_cht_complete(self._h, int(rid)), "xattn_cht_complete")
+
+    def form_batch(self, max_batch: int, max_missing: int):
+        out = np.zeros(max(int(max_batch), 1), dtype=np.int64)
+        n = ctypes.c_int32(0)
+        _check(lib().xattn_cht_form_batch(self._h, int(max_batch), int(max_missing), out.ctypes.data,
+                                          ctypes.byref(n)), "xattn_cht_form_batch")
+        return [int(x) for x in out[:n.value]]
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            lib().xattn_cht_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def beam_topk(beam_score, logprob, token, n_out, parent, token_out, score_out, stream=None):

@@ -345,6 +345,39 @@ xattn_status xattn_step_graph_launch(xattn_step_graph* graph, void* stream);
  * is still running. */
 xattn_status xattn_step_graph_destroy(xattn_step_graph* graph);
 
+/*
+ * HOST-SIDE batch former (Feather page, "Requests of a Feather Must Flock
+ * Together", Metodologia 1: requests as cumulative hashes over fixed-size
+ * token blocks, a working set of the active batch's hashes and a min-heap of
+ * waiting requests by missing count, best candidate in O(log W)). Groups of
+ * sequences it puts together share a prefix, which is what xattn_decode
+ * serves as one request with the sequences as its beams.
+ *  - A request's full blocks are hashed cumulatively (a trailing partial
+ *    block is ignored); block i is covered when an active request has the
+ *    same tokens over blocks 0..i. missing = full blocks not covered.
+ *  - best: the waiting request with the fewest missing blocks, ties to the
+ *    earliest inserted; (-1, -1) when none waits.
+ *  - form_batch: if nothing is active, admit the earliest waiting request;
+ *    then admit the best while its missing count <= max_missing and fewer
+ *    than max_batch requests are active. Writes the admitted ids, in order,
+ *    to out_ids (room for max_batch) and their number to *out_n.
+ * Request ids are caller-chosen, >= 0 and unique among live requests.
+ * admit takes a waiting request, complete an active one (which is then
+ * forgotten); anything else is XATTN_ERR_INVALID_ARG. Runs on the host and
+ * allocates host memory; one structure must not be used by two threads at
+ * once.
+ */
+typedef struct xattn_cht xattn_cht;  /* opaque */
+xattn_status xattn_cht_create(int32_t block_size, xattn_cht** cht);
+xattn_status xattn_cht_destroy(xattn_cht* cht);
+xattn_status xattn_cht_insert(xattn_cht* cht, int64_t request_id, const int32_t* tokens,
+                              int64_t n_tokens);
+xattn_status xattn_cht_best(xattn_cht* cht, int64_t* request_id, int64_t* missing);
+xattn_status xattn_cht_admit(xattn_cht* cht, int64_t request_id);
+xattn_status xattn_cht_complete(xattn_cht* cht, int64_t request_id);
+xattn_status xattn_cht_form_batch(xattn_cht* cht, int32_t max_batch, int64_t max_missing,
+                                  int64_t* out_ids, int32_t* out_n);
+
 /* Human-readable name of a status code (static storage). */
 const char* xattn_status_string(xattn_status status);
 

@@ -79,7 +79,7 @@ class BruteCht:
 
     def form_batch(self, max_batch: int, max_missing: int):
         out = []
-        if not self.active and self.waiting:
+        if not self.active and self.waiting and max_batch > 0:
             first = min(self.waiting, key=lambda w: self.seq[w])
             self.admit(first)
             out.append(first)
