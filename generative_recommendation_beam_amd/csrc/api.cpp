@@ -64,10 +64,12 @@ xattn_status check_dims(const xattn_dims* d) {
     return XATTN_ERR_INVALID_ARG;
   if (d->pipeline_stages != 0 && d->pipeline_stages != 2 && d->pipeline_stages != 4)
     return XATTN_ERR_INVALID_ARG;
-  if (d->key_groups < 0 || d->key_groups > 2) return XATTN_ERR_INVALID_ARG;
-  if (d->key_groups == 2 && d->pipeline_stages == 4) return XATTN_ERR_INVALID_ARG;  // LDS
+  if (d->key_groups < 0 || d->key_groups == 3 || d->key_groups > 4) return XATTN_ERR_INVALID_ARG;
+  if (d->key_groups == 4 && d->pipeline_stages == 4) return XATTN_ERR_INVALID_ARG;  // LDS
   if (!(d->scale == d->scale)) return XATTN_ERR_INVALID_ARG;  // NaN
   if (d->head_dim != 64 && d->head_dim != 128) return XATTN_ERR_UNSUPPORTED;
+  if (d->key_groups == 4 && d->head_dim != 128) return XATTN_ERR_UNSUPPORTED;
+  if (d->key_groups == 4 && d->rows_per_block == 128) return XATTN_ERR_UNSUPPORTED;  // 16 waves
   if (d->dtype != XATTN_F32 && d->dtype != XATTN_BF16) return XATTN_ERR_UNSUPPORTED;
   if (d->beam_width > kMaxBeamWidth) return XATTN_ERR_UNSUPPORTED;
   const int64_t nb = (int64_t)d->num_requests * d->beam_width;
@@ -103,11 +105,13 @@ Plan make_plan(const xattn_dims* d, int which) {
           (int64_t)d->num_requests * d->num_kv_heads * cdiv(M, rows) < kNumCUs &&
           maxP >= kKeyGroupMinKeys) {
         // Too few (request, kv head, row tile) workgroups to cover the CUs:
-        // halve the rows per workgroup and give each half of its waves
-        // alternate key tiles, so twice the workgroups run with the same
-        // waves each and every wave walks half the prompt.
+        // take 64 rows per workgroup and split the keys of those rows over
+        // wave groups, so twice the workgroups run and every wave walks a
+        // share of the prompt. Head dim 128 takes four groups (two waves per
+        // SIMD, which hides the loop's MFMA and LDS latency measured on
+        // MI355X); other head dims take two.
         rows = 64;
-        kg = 2;
+        kg = d->head_dim == 128 ? 4 : 2;
       }
       p.kgroups = kg;
       p.waves = rows / 32 * kg;

@@ -207,6 +207,44 @@ __device__ __forceinline__ void tile_step(const char* buf, int kbase, int vbase,
   half_softmax_pv<D, MASK>(buf, vbase, sacc[1], 1, oacc, m_run, l_part, c, hh, nvalid);
 }
 
+// One 32-key half (kb) of a 64-key tile for one wavefront: the S^T MFMAs of
+// that half, its online softmax and its P.V MFMAs (two key groups splitting
+// each tile between them).
+template <int D, bool MASK>
+__device__ __forceinline__ void half_tile_step(const char* buf, int kbase, int vbase, const bf16x8_t* qf,
+                                               f32x16_t* oacc, float& m_run, float& l_part, float c, int hh,
+                                               int nvalid, int kb) {
+  using TG = TileGeom<D>;
+  constexpr int NDC = D / 16;
+  f32x16_t sacc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+  bf16x8_t ka[NDC];
+  const char* kbuf = buf + kb * 32 * TG::ROWB;
+#pragma unroll
+  for (int dc = 0; dc < NDC; ++dc) ka[dc] = *reinterpret_cast<const bf16x8_t*>(kbuf + (kbase ^ (32 * dc)));
+  __builtin_amdgcn_sched_group_barrier(0x100, NDC, 0);
+#pragma unroll
+  for (int dc = 0; dc < NDC; ++dc) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc], qf[dc], sacc, 0, 0, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, NDC, 0);
+  half_softmax_pv<D, MASK>(buf, vbase, sacc, kb, oacc, m_run, l_part, c, hh, nvalid);
+}
+
+// Wait until at most n vector-memory operations are in flight. The counter
+// field needs an immediate (at most 63), so n is rounded down to a multiple
+// of 8 (a smaller count only waits longer).
+__device__ __forceinline__ void wait_vm_at_most(int n) {
+  if (n >= 63) __asm__ volatile("s_waitcnt vmcnt(63)" ::: "memory");
+  else if (n >= 56) __asm__ volatile("s_waitcnt vmcnt(56)" ::: "memory");
+  else if (n >= 48) __asm__ volatile("s_waitcnt vmcnt(48)" ::: "memory");
+  else if (n >= 40) __asm__ volatile("s_waitcnt vmcnt(40)" ::: "memory");
+  else if (n >= 32) __asm__ volatile("s_waitcnt vmcnt(32)" ::: "memory");
+  else if (n >= 24) __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else if (n >= 16) __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (n >= 8) __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // Wait until at most `ahead` tiles' loads (each `lpt` instructions per wave)
 // are still in flight. The counter field needs an immediate, hence the switch.
 // (The field holds at most 63; a smaller count only waits longer.)
@@ -320,9 +358,11 @@ __device__ __forceinline__ void store_rows(float* dst, const f32x16_t* oacc) {
 // ahead of split 0). NS = LDS pipeline stages (tiles in flight + 1).
 //
 // Key groups (KG = 2): the NW waves form KG groups of RG = NW/KG waves; each
-// group covers the same 32*RG query rows, and group kg takes the 64-key tiles
-// kg, kg+KG, ... of the range. Each step loads KG tiles (one super-tile) into
-// one LDS stage. At the end the groups' softmax states are combined through
+// group covers the same 32*RG query rows. With two LDS stages, group kg takes
+// the 64-key tiles kg, kg+KG, ... of the range and each step loads KG tiles
+// (one super-tile) into one stage. With four stages (which only fit for
+// 64-key steps) each step loads one tile and group kg takes its 32-key half
+// kg: half the work per step, three steps of loads in flight. At the end the groups' softmax states are combined through
 // LDS with the log-sum-exp rule; group kg then finalizes and stores column
 // blocks [kg*NDB/KG, (kg+1)*NDB/KG) of the head dim.
 template <int D, int NW, int NS, int KG>
@@ -331,16 +371,21 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   // The host pass only needs this kernel's signature for its launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
   using TG = TileGeom<D>;
-  using LP = LoadPlan<D, NW, KG>;
+  // Groups split tiles in halves: KG = 2 with four stages (one tile a step),
+  // or KG = 4 (two tiles a step, groups 2t and 2t+1 on tile t).
+  constexpr bool HALF = (KG == 2 && NS == 4) || KG == 4;
+  constexpr int TPS = KG == 4 ? 2 : (HALF ? 1 : KG);  // 64-key tiles per step
+  using LP = LoadPlan<D, NW, TPS>;
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
   constexpr int RG = NW / KG;          // row groups of 32 query rows
   constexpr int NDBW = NDB / KG;       // column blocks each wave finalizes
-  constexpr int ST = BN * KG;          // keys per super-tile
-  constexpr int SBUF = KG * TG::BUFB;  // LDS bytes per stage
+  constexpr int ST = BN * TPS;          // keys per step
+  constexpr int SBUF = TPS * TG::BUFB;  // LDS bytes per stage
   constexpr int LPT = 2 * LP::NJ;      // load instructions per super-tile per wave
-  static_assert(KG == 1 || KG == 2, "one or two key groups");
-  static_assert(KG == 1 || RG * NDB * 4096 + 2 * KG * RG * 32 * 4 <= NS * SBUF,
+  static_assert(KG == 1 || KG == 2 || KG == 4, "one, two or four key groups");
+  static_assert(NDB % KG == 0, "every key group finalizes whole column blocks");
+  static_assert(KG == 1 || RG * NDB * (KG - 1) * 4096 + 2 * KG * RG * 32 * 4 <= NS * SBUF,
                 "the key-group exchange must fit in the stage buffers");
   __shared__ __attribute__((aligned(1024))) char smem[NS * SBUF];
   __shared__ int s_last;
@@ -399,7 +444,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   // and every later load finds its super-tile already in L2, brought in by
   // the workgroup that started there. The last (possibly partial) super-tile
   // stays last. The softmax result does not depend on the order.
-  const int rot = (KG == 2 && nsup > 2) ? tile % (nsup - 1) : 0;
+  const int rot = (KG >= 2 && nsup > 2) ? tile % (nsup - 1) : 0;
   auto issue_tile = [&](int t) {
     lds_char* buf = lsm + (t % NS) * SBUF + wave * 1024;
     const int pt = t < nsup - 1 ? (t + rot) % (nsup - 1) : t;  // super-tile loaded at step t
@@ -513,9 +558,15 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   }
 
   // Wait for super-tile `it`, then refill the buffer super-tile it-1 used.
+  // The token rows (when fetched inside the loop) follow the loads of
+  // super-tile tok_after; whatever was issued after super-tile `it` may stay
+  // in flight.
+  int tok_after = -1;
   auto advance = [&](int it) {
     if (NPF > 0 && NS == 2 && it == 1)  // the token rows requested after tile 1's loads may stay in flight
       __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(NPF * (NDC + 4 * NDB)) : "memory");
+    else if (NPF > 0 && NS > 2)
+      wait_vm_at_most(min(issued - 1 - it, NS - 2) * LPT + (tok_after >= it ? NPF * (NDC + 4 * NDB) : 0));
     else
       wait_tiles<LPT>(min(issued - 1 - it, NS - 2));
     __syncthreads();  // super-tile `it` landed for every wave; it-1's buffer is free
@@ -527,21 +578,34 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   // This wave's tile of super-tile `it` sits at stage (it % NS), slot kg.
   for (int it = 0; it + 1 < nsup; ++it) {  // full super-tiles
     advance(it);
-    tile_step<D, false>(smem + (it % NS) * SBUF + kg * TG::BUFB, kbase, vbase, qf, oacc, m_run, l_part, c,
-                        hh, BN);
+    if constexpr (HALF)
+      half_tile_step<D, false>(smem + (it % NS) * SBUF + (kg >> 1) * (TPS - 1) * TG::BUFB, kbase, vbase, qf,
+                               oacc, m_run, l_part, c, hh, BN, TPS == 2 ? (kg & 1) : kg);
+    else
+      tile_step<D, false>(smem + (it % NS) * SBUF + kg * TG::BUFB, kbase, vbase, qf, oacc, m_run, l_part, c,
+                          hh, BN);
     if (NPF > 0 && it == 0) {
-      __asm__ volatile("" ::: "memory");  // keep these loads after tile 1's
+      __asm__ volatile("" ::: "memory");  // keep these loads after the tiles issued so far
       fetch_tokens();
+      tok_after = issued - 1;
     }
   }
   if (NPF > 0 && nsup <= 1) fetch_tokens();
   if (nsup > 0) {  // the last super-tile: this wave's tile may be partial or empty
     const int it = nsup - 1;
     advance(it);
-    const int nv = nkeys - (it * KG + kg) * BN;
-    if (nv > 0)
-      tile_step<D, true>(smem + (it % NS) * SBUF + kg * TG::BUFB, kbase, vbase, qf, oacc, m_run, l_part, c,
-                         hh, min(nv, BN));
+    if constexpr (HALF) {
+      const int sub = TPS == 2 ? (kg >> 1) : 0, half = TPS == 2 ? (kg & 1) : kg;
+      const int nv = nkeys - (it * TPS + sub) * BN;  // valid keys of this group's tile
+      if (nv > 32 * half)
+        half_tile_step<D, true>(smem + (it % NS) * SBUF + sub * TG::BUFB, kbase, vbase, qf, oacc, m_run, l_part,
+                                c, hh, min(nv, BN), half);
+    } else {
+      const int nv = nkeys - (it * KG + kg) * BN;
+      if (nv > 0)
+        tile_step<D, true>(smem + (it % NS) * SBUF + kg * TG::BUFB, kbase, vbase, qf, oacc, m_run, l_part, c,
+                           hh, min(nv, BN));
+    }
   }
 
   wait_vmem();  // every tile load has landed before the stage buffers are reused
@@ -564,53 +628,85 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
 
   float l_tot = l_part + __shfl_xor(l_part, 32);
   // own[j]: column block kg*NDBW + j of this wave's 32 rows, combined over
-  // the key groups.
+  // the key groups. Each group hands every other group the column blocks
+  // that group finalizes (KG - 1 slots per block), then merges the ones it
+  // owns with the log-sum-exp rule.
   f32x16_t own[NDBW];
   if constexpr (KG == 1) {
 #pragma unroll
     for (int j = 0; j < NDB; ++j) own[j] = oacc[j];
   } else {
-    float4* xo = reinterpret_cast<float4*>(smem);  // [RG][NDB][4][64] float4
-    float* xm = reinterpret_cast<float*>(smem + RG * NDB * 4096);
+    float4* xo = reinterpret_cast<float4*>(smem);  // [RG][NDB][KG-1][4][64] float4
+    float* xm = reinterpret_cast<float*>(smem + RG * NDB * (KG - 1) * 4096);
     float* xl = xm + KG * RG * 32;
+    auto slot = [&](int db, int src) {  // exchange slot of block db from group src
+      const int owner = db / NDBW;
+      return (rg * NDB + db) * (KG - 1) + (src < owner ? src : src - 1);
+    };
     __syncthreads();  // every wave is done reading the stage buffers
     if (hh == 0) {
       xm[(kg * RG + rg) * 32 + ql] = m_run;
       xl[(kg * RG + rg) * 32 + ql] = l_tot;
     }
-    // hand the other group the column blocks it finalizes
 #pragma unroll
-    for (int j = 0; j < NDBW; ++j) {
-      const int db = kg ? j : NDBW + j;
+    for (int db = 0; db < NDB; ++db) {
+      if (db / NDBW == kg) continue;  // uniform: this group's own block
+      const int sl = slot(db, kg);
 #pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        float4 v;
-        v.x = kg ? oacc[j][4 * ig + 0] : oacc[NDBW + j][4 * ig + 0];
-        v.y = kg ? oacc[j][4 * ig + 1] : oacc[NDBW + j][4 * ig + 1];
-        v.z = kg ? oacc[j][4 * ig + 2] : oacc[NDBW + j][4 * ig + 2];
-        v.w = kg ? oacc[j][4 * ig + 3] : oacc[NDBW + j][4 * ig + 3];
-        xo[((rg * NDB + db) * 4 + ig) * 64 + lane] = v;
-      }
+      for (int ig = 0; ig < 4; ++ig)
+        xo[(sl * 4 + ig) * 64 + lane] =
+            make_float4(oacc[db][4 * ig], oacc[db][4 * ig + 1], oacc[db][4 * ig + 2], oacc[db][4 * ig + 3]);
     }
     __syncthreads();
-    const int og = ((1 - kg) * RG + rg) * 32 + ql;
-    const float mo = xm[og];
-    const float lo = xl[og];
-    const float mn = fmaxf(m_run, mo);
-    const float as = m_run == neg_inf() ? 0.f : exp2_approx(m_run - mn);
-    const float ao = mo == neg_inf() ? 0.f : exp2_approx(mo - mn);
-    l_tot = l_tot * as + lo * ao;
+    float mg[KG], lg[KG];
+    float mn = neg_inf();
+#pragma unroll
+    for (int g = 0; g < KG; ++g) {
+      mg[g] = xm[(g * RG + rg) * 32 + ql];
+      lg[g] = xl[(g * RG + rg) * 32 + ql];
+      mn = fmaxf(mn, mg[g]);
+    }
+    float ag[KG];
+    float lsum = 0.f;
+#pragma unroll
+    for (int g = 0; g < KG; ++g) {
+      ag[g] = mg[g] == neg_inf() ? 0.f : exp2_approx(mg[g] - mn);
+      lsum += lg[g] * ag[g];
+    }
+    l_tot = lsum;
     m_run = mn;
+    // this wave's own blocks: select them out of oacc (kg is only known at
+    // run time; a select chain keeps oacc in registers)
 #pragma unroll
     for (int j = 0; j < NDBW; ++j) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float v = oacc[j][i];
+#pragma unroll
+        for (int g = 1; g < KG; ++g) v = kg == g ? oacc[g * NDBW + j][i] : v;
+        own[j][i] = v;
+      }
+    }
+    float aself = ag[0];
+#pragma unroll
+    for (int g = 1; g < KG; ++g) aself = kg == g ? ag[g] : aself;
+#pragma unroll
+    for (int j = 0; j < NDBW; ++j) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) own[j][i] *= aself;
       const int db = kg * NDBW + j;
 #pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        const float4 v = xo[((rg * NDB + db) * 4 + ig) * 64 + lane];
-        own[j][4 * ig + 0] = (kg ? oacc[NDBW + j][4 * ig + 0] : oacc[j][4 * ig + 0]) * as + v.x * ao;
-        own[j][4 * ig + 1] = (kg ? oacc[NDBW + j][4 * ig + 1] : oacc[j][4 * ig + 1]) * as + v.y * ao;
-        own[j][4 * ig + 2] = (kg ? oacc[NDBW + j][4 * ig + 2] : oacc[j][4 * ig + 2]) * as + v.z * ao;
-        own[j][4 * ig + 3] = (kg ? oacc[NDBW + j][4 * ig + 3] : oacc[j][4 * ig + 3]) * as + v.w * ao;
+      for (int g = 0; g < KG; ++g) {
+        if (g == kg) continue;  // uniform
+        const int sl = slot(db, g);
+#pragma unroll
+        for (int ig = 0; ig < 4; ++ig) {
+          const float4 v = xo[(sl * 4 + ig) * 64 + lane];
+          own[j][4 * ig + 0] += v.x * ag[g];
+          own[j][4 * ig + 1] += v.y * ag[g];
+          own[j][4 * ig + 2] += v.z * ag[g];
+          own[j][4 * ig + 3] += v.w * ag[g];
+        }
       }
     }
   }
@@ -714,10 +810,14 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
 
 template <int D, int NW, int KG>
 hipError_t launch_dwk(const SharedMfmaArgs& a, int64_t grid, int64_t n_logical, hipStream_t st) {
-  if (KG == 1 && a.stages == 4)
-    hipLaunchKernelGGL((shared_mfma_kernel<D, NW, 4, 1>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a, n_logical);
-  else
-    hipLaunchKernelGGL((shared_mfma_kernel<D, NW, 2, KG>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a, n_logical);
+  if constexpr (KG != 4) {
+    if (a.stages == 4) {
+      hipLaunchKernelGGL((shared_mfma_kernel<D, NW, 4, KG>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a,
+                         n_logical);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((shared_mfma_kernel<D, NW, 2, KG>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a, n_logical);
   return hipGetLastError();
 }
 
@@ -727,6 +827,13 @@ hipError_t launch_d(const SharedMfmaArgs& a, hipStream_t st) {
   const int64_t n_logical = (int64_t)a.s.R * a.s.Hkv * members * a.row_tiles;
   if (n_logical == 0) return hipSuccess;
   const int64_t grid = (n_logical + 7) / 8 * 8;
+  if (a.key_groups == 4) {
+    if constexpr (D == 128) {
+      if (a.waves == 4) return launch_dwk<D, 4, 4>(a, grid, n_logical, st);
+      return launch_dwk<D, 8, 4>(a, grid, n_logical, st);
+    }
+    return hipErrorInvalidValue;
+  }
   if (a.key_groups == 2) {
     switch (a.waves) {
       case 2: return launch_dwk<D, 2, 2>(a, grid, n_logical, st);

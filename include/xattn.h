@@ -88,10 +88,15 @@ typedef struct {
   int32_t rows_per_block;   /* 0 = automatic; else 32, 64 or 128 query rows per
                                Shared-stage workgroup (bf16 MFMA path) */
   int32_t pipeline_stages;  /* 0 = automatic; else 2 or 4 K/V tiles staged in LDS */
-  int32_t key_groups;       /* 0 = automatic; else 1 or 2 wavefront groups per
-                               Shared-stage workgroup that take alternate 64-key
-                               tiles of the same query rows (merged in LDS);
-                               2 requires pipeline_stages 2 */
+  int32_t key_groups;       /* 0 = automatic; else 1, 2 or 4 wavefront groups
+                               per Shared-stage workgroup that split the keys of
+                               the same query rows (merged in LDS). Two groups
+                               with 2 stages take alternate 64-key tiles, with 4
+                               stages the two 32-key halves of every tile. Four
+                               groups (head_dim 128, 32 or 64 rows, 2 stages
+                               only; else XATTN_ERR_UNSUPPORTED, or
+                               XATTN_ERR_INVALID_ARG for 4 stages) take the
+                               32-key halves of two 64-key tiles per step */
 } xattn_dims;
 
 /* Launch plan chosen for a dims (introspection for tests and tuning). */

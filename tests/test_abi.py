@@ -66,7 +66,9 @@ def _decode(d, ws=None, nbytes=0, **over):
     (dict(scale=float("nan")), xattn.XATTN_ERR_INVALID_ARG),
     (dict(B=20000), xattn.XATTN_ERR_UNSUPPORTED),
     (dict(key_groups=3), xattn.XATTN_ERR_INVALID_ARG),
-    (dict(key_groups=2, pipeline_stages=4), xattn.XATTN_ERR_INVALID_ARG),
+    (dict(key_groups=4, pipeline_stages=4), xattn.XATTN_ERR_INVALID_ARG),
+    (dict(key_groups=4, D=64), xattn.XATTN_ERR_UNSUPPORTED),
+    (dict(key_groups=4, rows_per_block=128), xattn.XATTN_ERR_UNSUPPORTED),
     (dict(rows_per_block=96), xattn.XATTN_ERR_INVALID_ARG),
 ])
 def test_invalid_dims_rejected(L, over, code):
@@ -97,8 +99,11 @@ def test_plan_introspection(L):
     p = xattn.get_plan(d, 2)
     assert p["mfma"] == 1 and p["rows_per_block"] in (32, 64, 128)
     # 8 x 4 (request, kv head) pairs x 4 row tiles of 128 would leave CUs idle:
-    # the plan halves the rows per workgroup and splits each one's keys in two
-    assert p["key_groups"] == 2 and p["rows_per_block"] == 64 and p["row_tiles"] == 8
+    # the plan halves the rows per workgroup and splits each one's keys over
+    # four wave groups (head dim 128), or two (head dim 64)
+    assert p["key_groups"] == 4 and p["rows_per_block"] == 64 and p["row_tiles"] == 8
+    p64 = xattn.get_plan(dims(R=8, B=128, Hq=16, Hkv=4, D=64, max_prefix_len=1024, max_unshared_len=3), 2)
+    assert p64["key_groups"] == 2 and p64["rows_per_block"] == 64
     assert xattn.get_plan(dims(R=8, B=128, Hq=16, Hkv=4, max_prefix_len=1024, max_unshared_len=3,
                                key_groups=1), 2)["rows_per_block"] == 128
     assert p["prefix_chunk"] % 64 == 0 and p["prefix_splits"] * p["prefix_chunk"] >= 1024

@@ -87,14 +87,21 @@ KG_CASES = ["ragged_small_bf16", "mfma_multi_tile", "d64_bf16", "g8_bf16", "g6_b
 
 
 @pytest.mark.parametrize("name", KG_CASES)
-@pytest.mark.parametrize("rows,ps", [(64, 0), (128, 0), (32, 0), (64, 3)])
-def test_decode_key_groups(name, rows, ps):
-    """Two wave groups per workgroup take alternate key tiles of the same rows
-    (prompts here end inside either group's tile, or leave one group none)."""
-    w = make_workload(name, seed_key=(305, rows, ps, zlib.crc32(name.encode()) % 1000), **CASES[name])
-    d, o, lse = run_decode(w, rows_per_block=rows, key_groups=2, prefix_splits=ps)
+@pytest.mark.parametrize("rows,ps,stages,kg", [(64, 0, 2, 2), (128, 0, 2, 2), (32, 0, 2, 2), (64, 3, 2, 2),
+                                               (64, 0, 4, 2), (128, 0, 4, 2), (32, 0, 4, 2), (64, 3, 4, 2),
+                                               (64, 0, 2, 4), (32, 0, 2, 4), (64, 3, 2, 4)])
+def test_decode_key_groups(name, rows, ps, stages, kg):
+    """Wave groups per workgroup split the keys of the same rows: two groups
+    on alternate 64-key tiles (2 stages) or on the two halves of every tile
+    (4 stages); four groups on the halves of two tiles a step. Prompts here
+    end inside any group's share, or leave some groups none."""
+    if kg == 4 and CASES[name]["D"] != 128:
+        pytest.skip("four key groups: head dim 128 only")
+    w = make_workload(name, seed_key=(305, rows, ps, kg, zlib.crc32(name.encode()) % 1000), **CASES[name])
+    d, o, lse = run_decode(w, rows_per_block=rows, key_groups=kg, prefix_splits=ps, pipeline_stages=stages)
     plan = xattn.get_plan(d.dims, 2)
-    assert plan["mfma"] == 1 and plan["key_groups"] == 2 and plan["rows_per_block"] == rows
+    assert plan["mfma"] == 1 and plan["key_groups"] == kg and plan["rows_per_block"] == rows
+    assert plan["pipeline_stages"] == stages
     O, L = oa.attention(w)
     compare(o, O, lse, L, w.dtype, f"decode key groups {name} plan={plan}")
 
