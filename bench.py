@@ -39,7 +39,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3       # fp32 vector
 
-DEFAULT_LAYERS = {"1": 1, "2": 16, "3": 6, "4A": 3, "4B": 2, "5": 2}
+DEFAULT_LAYERS = {"1": 16, "2": 16, "3": 6, "4A": 3, "4B": 2, "5": 2}
 WORKLOAD_NAMES = {
     "1": "tiny fp32: R=1 P=256 B=4 L=2 4q/1kv D=64",
     "2": "GR semantic-ID decode: R=8 P=1024 B=128 L=3 16q/4kv D=128 bf16",

@@ -13,6 +13,11 @@
 // costs one 16-lane shuffle reduction per query row. Each slot keeps its own
 // online-softmax state (max, sum, output) over the keys it saw; the 4 slots
 // are combined at the end with the same log-sum-exp rule as the Merge stage.
+//
+// Keys go in batches of U steps (4U keys): the K/V rows of a whole batch are
+// requested before any of them is used, and the slot indices of the next
+// batch of generated tokens are requested beside the current batch's rows,
+// so a wave waits one memory round trip per batch rather than per step.
 #include "device.h"
 #include "kernels.h"
 
@@ -39,16 +44,10 @@ struct ValuState {
     }
   }
 
-  // One step over the 4 keys held by the 4 slots. krow / vrow point to this
-  // lane's D/16 elements of its slot's key; `valid` is uniform per slot.
-  __device__ __forceinline__ void step(const T* krow, const T* vrow, bool valid) {
-    float kv[EPL], vv[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) kv[e] = vv[e] = 0.f;
-    if (valid) {
-      Load<T, EPL>::run(krow, kv);
-      Load<T, EPL>::run(vrow, vv);
-    }
+  // One step over the 4 keys held by the 4 slots: kv / vv are this lane's
+  // D/16 elements of its slot's key and value rows; `valid` is uniform per
+  // slot.
+  __device__ __forceinline__ void update(const float* kv, const float* vv, bool valid) {
     float s[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -103,6 +102,12 @@ template <typename T, int D, int NG>
 __global__ __launch_bounds__(kValuWaves * 64) void valu_attn_kernel(ValuArgs a, int64_t n_units,
                                                                     int ngroups) {
   constexpr int EPL = D / 16;
+  // Steps per batch: 64 dwords of K/V rows in flight per lane at most (32
+  // with 8 query heads, whose state takes twice the registers), 8 steps at
+  // most.
+  constexpr int STEP_DW = 2 * EPL * (int)sizeof(T) / 4;
+  constexpr int BUF_DW = NG >= 8 ? 32 : 64;
+  constexpr int U = BUF_DW / STEP_DW < 8 ? BUF_DW / STEP_DW : 8;
   const int lane = threadIdx.x & 63;
   const int64_t unit = (int64_t)blockIdx.x * kValuWaves + (threadIdx.x >> 6);
   if (unit >= n_units) return;  // uniform per wavefront
@@ -148,11 +153,16 @@ __global__ __launch_bounds__(kValuWaves * 64) void valu_attn_kernel(ValuArgs a, 
     }
     const T* kb = static_cast<const T*>(a.k_shared) + ((int64_t)h * s.n_ptok + a.prefix_off[r]) * D + dl * EPL;
     const T* vb = static_cast<const T*>(a.v_shared) + ((int64_t)h * s.n_ptok + a.prefix_off[r]) * D + dl * EPL;
-    for (int j0 = k0; j0 < k1; j0 += 4) {
-      const int j = j0 + slot_id;
-      const bool valid = j < k1;
-      const int jj = valid ? j : k0;
-      st.step(kb + (int64_t)jj * D, vb + (int64_t)jj * D, valid);
+    for (int j0 = k0; j0 < k1; j0 += 4 * U) {
+      float kv[U][EPL], vv[U][EPL];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {  // keys past k1 read row k1-1 and are skipped
+        const int64_t jj = min(j0 + 4 * u + slot_id, k1 - 1);
+        Load<T, EPL>::run(kb + jj * D, kv[u]);
+        Load<T, EPL>::run(vb + jj * D, vv[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) st.update(kv[u], vv[u], j0 + 4 * u + slot_id < k1);
     }
   }
   if (a.use_gen) {
@@ -162,15 +172,27 @@ __global__ __launch_bounds__(kValuWaves * 64) void valu_attn_kernel(ValuArgs a, 
       t0 = split * a.chunk;
       t1 = min(L, t0 + a.chunk);
     }
-    const int32_t* trow = a.slot_table + n * s.T_max;
-    const T* kp = static_cast<const T*>(a.k_pool);
-    const T* vp = static_cast<const T*>(a.v_pool);
-    for (int j0 = t0; j0 < t1; j0 += 4) {
-      const int j = j0 + slot_id;
-      const bool valid = j < t1;
-      const int64_t slot = valid ? (int64_t)trow[j] : 0;
-      const int64_t off = (slot * s.Hkv + h) * D + dl * EPL;
-      st.step(kp + off, vp + off, valid);
+    if (t1 > t0) {
+      const int32_t* trow = a.slot_table + n * s.T_max;
+      const T* kp = static_cast<const T*>(a.k_pool) + h * D + dl * EPL;
+      const T* vp = static_cast<const T*>(a.v_pool) + h * D + dl * EPL;
+      const int64_t tok_stride = (int64_t)s.Hkv * D;
+      // Tokens past t1 read the slot of token t1-1 and are skipped.
+      int slot[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) slot[u] = trow[min(t0 + 4 * u + slot_id, t1 - 1)];
+      for (int j0 = t0; j0 < t1; j0 += 4 * U) {
+        float kv[U][EPL], vv[U][EPL];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          Load<T, EPL>::run(kp + slot[u] * tok_stride, kv[u]);
+          Load<T, EPL>::run(vp + slot[u] * tok_stride, vv[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) slot[u] = trow[min(j0 + 4 * U + 4 * u + slot_id, t1 - 1)];
+#pragma unroll
+        for (int u = 0; u < U; ++u) st.update(kv[u], vv[u], j0 + 4 * u + slot_id < t1);
+      }
     }
   }
   st.combine_slots();

@@ -235,6 +235,22 @@ def test_append_large_beam_column_chunks():
     assert np.array_equal(kp, kpool) and np.array_equal(vp, vpool)
 
 
+def test_append_long_rows_column_chunks():
+    """Small B with long rows: each request's table spans two column chunks,
+    the second one ragged, and t crosses the chunk boundary during the run."""
+    w = make_workload("appL", R=2, B=5, Hq=2, Hkv=1, D=64, prefix_len=1, unshared_len=[450, 300],
+                      seed_key=(311, 0), parent_dist="uniform", T_max=450)
+    d = dv.upload(w)
+    dv.build_cache(d)
+    torch.cuda.synchronize()
+    kpool, vpool, table, ulen = _oracle_append(w)
+    assert np.array_equal(_np(d.table).astype(np.int64), table)
+    assert np.array_equal(_np(d.unshared_len)[:w.R], ulen)
+    kp = _np(d.k_pool.view(torch.int16)).view(np.uint16)
+    vp = _np(d.v_pool.view(torch.int16)).view(np.uint16)
+    assert np.array_equal(kp, kpool) and np.array_equal(vp, vpool)
+
+
 def test_append_on_full_row_changes_nothing():
     """An append on requests whose rows are full writes nothing and leaves the
     lengths as they are (every workgroup still arrives once)."""
