@@ -277,15 +277,6 @@ struct NonShared {
   const uint16_t* vp;
   int hkv;
 
-  __device__ __forceinline__ void init(const SharedMfmaArgs& a, int r, int h, int bq, int kg_, int hh) {
-    const Shape& s = a.s;
-    kg = kg_;
-    L = __builtin_amdgcn_readfirstlane(a.unshared_len[r]);
-    hkv = s.Hkv;
-    kp = a.k_pool + (int64_t)h * D + 8 * hh;
-    vp = a.v_pool + (int64_t)h * D + 4 * hh;
-    trow = a.slot_table + ((int64_t)r * s.B + bq) * s.T_max;
-  }
   // Does this wave take a u-th token (token kg + KG*u)?
   __device__ __forceinline__ bool has(int u) const { return kg + KG * u < L; }
   __device__ __forceinline__ int slot(int u) const { return has(u) ? trow[kg + KG * u] : 0; }
@@ -416,11 +407,54 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   const int hh = lane >> 5;
   const int ql = lane & 31;
 
+  // Query rows, the per-request values (prompt length and offset, generated
+  // length) and the first slot cells are requested together, before
+  // anything waits. The per-request values go through vector loads (an index
+  // the compiler cannot prove uniform): as scalar loads each would wait for
+  // the one before it, the scalar cache returning out of order.
+  // Rows past the last query row compute on a copy of that row (their
+  // columns of S^T and O^T are independent of the others) and store nothing.
+  const int row = tile * (RG * 32) + rg * 32 + ql;
+  const bool row_ok = row < M;
+  const int rowc = min(row, M - 1);
+  const int bq = rowc / G;
+  const int gq = rowc - bq * G;
+  const int64_t qrow = ((int64_t)r * s.B + bq) * s.Hq + h * G + gq;
+  // Non-Shared tokens: in the generated-token member, or (no such member) in
+  // prompt split 0. They are folded in after the prompt tiles.
+  const bool do_ns = a.k_pool != nullptr && (gen_only || (!a.gen_member && member == 0));
+  // With one workgroup per CU and registers to spare, the first NPF tokens'
+  // K/V rows are requested right after the first super-tile's compute, so
+  // they have landed by the end of the loop; the others are fetched after
+  // the loop, the first slot cell already in hand.
+  constexpr int NPF = (NS * SBUF > 80 * 1024 && NW <= 4) ? 2 : 0;
+  constexpr int NSL = NPF > 0 ? NPF : 1;
+  int zv;
+  __asm__ volatile("v_mov_b32 %0, 0" : "=v"(zv));
+  const int Pv = a.prefix_len[r + zv];
+  const int64_t poffv = a.prefix_off[r + zv];
+  // Branch-free (a branch here would make the compiler wait for these reads
+  // where the paths join): without Non-Shared tokens the reads go to
+  // prefix_len[0], which always exists; slot cells are clamped to the row
+  // and ignored beyond the length.
+  const int32_t* lenp = do_ns ? a.unshared_len + r : a.prefix_len;
+  const int32_t* trow = do_ns ? a.slot_table + ((int64_t)r * s.B + bq) * s.T_max : a.prefix_len;
+  const int tlast = do_ns ? s.T_max - 1 : 0;
+  const int lenv = lenp[zv];
+  int pslot[NSL];
+#pragma unroll
+  for (int u = 0; u < NSL; ++u) pslot[u] = trow[min(kg + KG * u, tlast)];
+  bf16x8_t qf[NDC];
+  {
+    const uint16_t* qp = a.q + qrow * D + 8 * hh;
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) qf[dc] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + 16 * dc));
+  }
+
   // Per-request values are the same for the whole workgroup.
-  const int P = __builtin_amdgcn_readfirstlane(a.prefix_len[r]);
-  const int64_t poff = a.prefix_off[r];
-  const int64_t poff_u = ((int64_t)__builtin_amdgcn_readfirstlane((int)(poff >> 32)) << 32) |
-                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(poff & 0xffffffff));
+  const int P = __builtin_amdgcn_readfirstlane(Pv);
+  const int64_t poff_u = ((int64_t)__builtin_amdgcn_readfirstlane((int)(poffv >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(poffv & 0xffffffff));
   const int64_t kvbase = ((int64_t)h * s.n_ptok + poff_u) * D;
   const uint16_t* Kg = a.k_shared + kvbase;
   const uint16_t* Vg = a.v_shared + kvbase;
@@ -455,58 +489,15 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, buf + LP::lds_off(j) + TG::TILEB, 16, lp.v[j], tile_bytes, 0, 0);
     }
   };
-  // Query rows and slot indices are requested first, so that nothing waits
-  // on the prompt tiles to reach them; super-tiles 0 .. NS-2 follow.
-  // Rows past the last query row compute on a copy of that row (their
-  // columns of S^T and O^T are independent of the others) and store nothing.
-  const int row = tile * (RG * 32) + rg * 32 + ql;
-  const bool row_ok = row < M;
-  const int rowc = min(row, M - 1);
-  const int bq = rowc / G;
-  const int gq = rowc - bq * G;
-  const int64_t qrow = ((int64_t)r * s.B + bq) * s.Hq + h * G + gq;
-
-  bf16x8_t qf[NDC];
-  {
-    const uint16_t* qp = a.q + qrow * D + 8 * hh;
-#pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) qf[dc] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + 16 * dc));
-  }
-  // Non-Shared tokens: in the generated-token member, or (no such member) in
-  // prompt split 0. They are folded in after the prompt tiles. With one
-  // workgroup per CU (registers to spare, nothing else to hide latency
-  // behind) the length and the first NPF tokens' slot cells are read with
-  // the query rows, and those tokens' K/V rows are requested right after the
-  // first super-tile's compute, so that none of this chain holds up the
-  // tiles; otherwise everything is fetched after the loop while the CU's
-  // other workgroup computes.
-  const bool do_ns = a.k_pool != nullptr && (gen_only || (!a.gen_member && member == 0));
-  constexpr int NPF = (NS * SBUF > 80 * 1024 && NW <= 4) ? 2 : 0;
   NonShared<D, KG> ns;
-  ns.L = 0;
+  ns.L = do_ns ? __builtin_amdgcn_readfirstlane(lenv) : 0;
   ns.kg = kg;
-  int pslot[NPF > 0 ? NPF : 1];
+  ns.hkv = s.Hkv;
+  ns.kp = do_ns ? a.k_pool + (int64_t)h * D + 8 * hh : a.q;
+  ns.vp = do_ns ? a.v_pool + (int64_t)h * D + 4 * hh : a.q;
+  ns.trow = trow;
   uint4 pk[NPF > 0 ? NPF : 1][NDC];
   uint2 pv[NPF > 0 ? NPF : 1][NDB][4];
-  if (NPF > 0) {
-    // Branch-free (a branch here would make the compiler wait for these
-    // reads where the paths join): without Non-Shared tokens the reads go
-    // to prefix_len[0], which always exists; slot cells are clamped to the
-    // row and masked to slot 0 once the length is known.
-    const int32_t* lenp = do_ns ? a.unshared_len + r : a.prefix_len;
-    const int32_t* trow = do_ns ? a.slot_table + ((int64_t)r * s.B + bq) * s.T_max : a.prefix_len;
-    const int tlast = do_ns ? s.T_max - 1 : 0;
-    const int len = *lenp;
-#pragma unroll
-    for (int u = 0; u < NPF; ++u) pslot[u] = trow[min(kg + KG * u, tlast)];
-    ns.L = do_ns ? __builtin_amdgcn_readfirstlane(len) : 0;
-    ns.hkv = s.Hkv;
-    ns.kp = do_ns ? a.k_pool + (int64_t)h * D + 8 * hh : a.q;
-    ns.vp = do_ns ? a.v_pool + (int64_t)h * D + 4 * hh : a.q;
-    ns.trow = trow;
-  } else if (do_ns) {
-    ns.init(a, r, h, bq, kg, hh);
-  }
   // K/V rows of the first NPF tokens (missing ones read slot 0 / the first
   // query row, in bounds either way).
   auto fetch_tokens = [&]() {
@@ -616,7 +607,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   for (int u = 0; u < NPF; ++u)
     if (ns.has(u)) token_update<D>(pk[u], pv[u], qf, oacc, m_run, l_part, c, hh);
   if (ns.has(NPF)) {
-    int sl = ns.slot(NPF);
+    int sl = NPF == 0 ? pslot[0] : ns.slot(NPF);
     for (int u = NPF; u < NonShared<D, KG>::NT && ns.has(u); ++u) {
       uint4 kk[NDC];
       uint2 vv[NDB][4];

@@ -106,6 +106,25 @@ def test_decode_key_groups(name, rows, ps, stages, kg):
     compare(o, O, lse, L, w.dtype, f"decode key groups {name} plan={plan}")
 
 
+@pytest.mark.parametrize("rows,kg", [(64, 4), (32, 4), (64, 2)])
+def test_decode_late_score_jump(rows, kg):
+    """Keys 40 and 41 of a 300-key prompt score ~130 log2 units above every
+    other key, for every query row, and arrive after other keys of the same
+    group have set its running maximum: the accumulated output must be
+    rescaled by about 2^-127 without losing the later keys' weights."""
+    w = make_workload("jump", R=1, B=16, Hq=8, Hkv=2, D=128, prefix_len=[300], unshared_len=[2],
+                      seed_key=(312, rows, kg))
+    w.q[:] = 0x3F80                      # bf16 1.0: a query row's score is its key's row sum
+    w.k_shared[:, 40, :] = 0x4100        # bf16 8.0: score 1024 * scale
+    w.k_shared[:, 41, :] = 0x4100
+    w.k_shared[:, 41, :8] = 0x40E0       # bf16 7.0: score 1016 * scale, a visible second weight
+    d, o, lse = run_decode(w, rows_per_block=rows, key_groups=kg)
+    plan = xattn.get_plan(d.dims, 2)
+    assert plan["key_groups"] == kg and plan["rows_per_block"] == rows
+    O, L = oa.attention(w)
+    compare(o, O, lse, L, "bf16", f"late score jump plan={plan}")
+
+
 @pytest.mark.parametrize("name", ["ragged_small_bf16", "mfma_multi_tile", "b1_decode_bf16", "f32_small"])
 @pytest.mark.parametrize("ps", [0, 3])
 @pytest.mark.parametrize("kg", [0, 2])
