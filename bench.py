@@ -1,10 +1,11 @@
 """Benchmark: staged beam-search decode attention on one MI355X.
 
 One step = one decode step: xattn_beam_topk picks each request's surviving
-beams from its beam_width x top_k candidate pool, then per layer
-xattn_cache_append of the step's new tokens (token-granular K/V write and
-slot-table rewrite, with the selected parents) and xattn_decode, on n_layers
-distinct layer buffers (distinct Q, prompt KV,
+beams from its beam_width x top_k candidate pool, then per layer the cache
+append of the step's new tokens (token-granular K/V write and slot-table
+rewrite, with the selected parents) and the decode, as one
+xattn_append_decode call (ping-pong tables; the append folds into the decode
+launch), on n_layers distinct layer buffers (distinct Q, prompt KV,
 Non-Shared pool, slot tables and lengths per layer, so the working set
 defeats the 256 MB Infinity Cache). By default the whole step is one
 captured HIP graph (xattn_step_graph_*), launched once per step; --eager
@@ -18,11 +19,13 @@ work.
 
 Prints ONE JSON line. Metric: beams * layer-steps per second, plus achieved
 HBM bandwidth on algorithmic bytes (unique KV: prompt KV once per request,
-generated KV once per beam) and the roofline of the dominant kernel (the
-decode). Its per-launch duration comes from HIP events: around every decode
-call of the timed steps with --eager; in graph mode, around K launches of a
-graph of every layer's decode, right after the timed steps (events cannot be
-recorded inside a captured graph on the runtime PyTorch ships).
+generated KV once per beam; plus the append's new rows and table cells) and
+the roofline of the dominant kernel (the fused append + decode launch). Its
+per-launch duration comes from HIP events: around every call of the timed
+steps with --eager; in graph mode, around K launches of a graph of every
+layer's call, right after the timed steps, each after the lengths are
+restored (events cannot be recorded inside a captured graph on the runtime
+PyTorch ships).
 """
 from __future__ import annotations
 
@@ -118,7 +121,7 @@ def cpu_baseline(layers_np, min_seconds=10.0):
                        f"of the same workload (fp64 numpy oracle, {used} worker processes, {el:.1f} s)")
 
 
-def paged_baseline(layers, K, xattn_call_us, xattn_step_ms):
+def paged_baseline(layers, K, xattn_decode_us, xattn_call_us, xattn_step_ms):
     """The same layers in a PagedAttention-style block-paged cache: per layer,
     the copies branching beams make of their partial tail blocks, then the
     per-beam paged decode. HIP events around every call, K rounds, queued
@@ -157,11 +160,14 @@ def paged_baseline(layers, K, xattn_call_us, xattn_step_ms):
     pc0 = paged[0][1]
     return dict(decode_us_per_call=round(dec_us, 2), block_copy_us_per_call=round(copy_us, 2),
                 step_ms=round(step_ms, 4), blocks_per_layer=int(pc0.k_cache.shape[0]),
-                decode_speedup_xattn=round(dec_us / xattn_call_us, 2),
+                decode_speedup_xattn=round(dec_us / xattn_decode_us, 2),
+                layer_speedup_xattn=round((copy_us + dec_us) / xattn_call_us, 2),
                 step_speedup_xattn=round(step_ms / xattn_step_ms, 2),
                 note="same layers, same attention; PagedAttention-style per-beam paged decode "
                      "(16-token blocks, prompt blocks shared and re-read by every beam) plus the "
-                     "copy each beam makes of its parent's tail block; eager launches")
+                     "copy each beam makes of its parent's tail block; eager launches. "
+                     "decode_speedup_xattn: against xattn's decode alone; layer_speedup_xattn: "
+                     "copy + decode against the fused append + decode call")
 
 
 def batch_former_timing():
@@ -310,7 +316,7 @@ def main():
                       pipeline_stages=args.stages, key_groups=args.key_groups)
         d.unshared_len = ulen_all[l]
         table_in, table_out, t_last = dv.prepare_step(d)
-        o, lse, ws, nb = dv.alloc_outputs(d, 2)
+        o, lse, ws, nb = dv.alloc_outputs(d, 3 if t_last is not None else 2)
         layers.append((d, o, lse, ws, nb, table_in, table_out, t_last))
     ulen0 = ulen_all.clone()
     # The step opens with the survivor selection (beam width x top-k pool per
@@ -334,12 +340,17 @@ def main():
         ulen_all.copy_(ulen0)
         xattn.beam_topk(*sel_in, w0.B, sel_parent, sel_tok, sel_score)
         for (d, o, lse, ws, nb, tin, tout, t_last), (e0, e1) in zip(layers, evs):
-            if t_last is not None:
-                xattn.cache_append(d.dims, d.k_new[t_last], d.v_new[t_last], sel_parent, d.slot_base,
-                                   d.active[t_last], d.k_pool, d.v_pool, tin, tout, d.unshared_len)
             e0.record()
-            xattn.decode(d.dims, d.q, d.k_shared, d.v_shared, d.prefix_off, d.prefix_len, d.k_pool,
-                         d.v_pool, tout, d.unshared_len, o, lse, ws if nb else None, nb)
+            if t_last is not None:
+                xattn.append_decode(d.dims, q=d.q, k_shared=d.k_shared, v_shared=d.v_shared,
+                                    prefix_off=d.prefix_off, prefix_len=d.prefix_len, k_new=d.k_new[t_last],
+                                    v_new=d.v_new[t_last], parent=sel_parent, slot_base=d.slot_base,
+                                    active=d.active[t_last], k_pool=d.k_pool, v_pool=d.v_pool, table_in=tin,
+                                    table_out=tout, unshared_len=d.unshared_len, o=o, lse=lse,
+                                    workspace=ws if nb else None, workspace_bytes=nb)
+            else:
+                xattn.decode(d.dims, d.q, d.k_shared, d.v_shared, d.prefix_off, d.prefix_len, d.k_pool,
+                             d.v_pool, tout, d.unshared_len, o, lse, ws if nb else None, nb)
             e1.record()
 
     step_evs = [new_events() for _ in range(K)] if args.eager else []
@@ -355,9 +366,11 @@ def main():
         step_graph = xattn.StepGraph(steps, select=select)
         select_graph = xattn.StepGraph([], select=xattn.beam_select(*sel_in, w0.B, sel_parent, sel_tok,
                                                                     sel_score))
-        # Every layer's decode alone, back to back in one graph, to time the
-        # decode kernel with HIP events around its launches (the runtime
-        # PyTorch ships cannot record events inside a captured graph).
+        # Every layer's call alone, back to back in one graph, to time the
+        # dominant kernel with HIP events around its launches (the runtime
+        # PyTorch ships cannot record events inside a captured graph); and
+        # the plain decodes on the complete caches, for reference.
+        layer_graph = xattn.StepGraph(steps)
         decode_graph = xattn.StepGraph([dv.layer_step(d, o, lse, ws, nb, None, tout, None)
                                         for (d, o, lse, ws, nb, tin, tout, t_last) in layers])
         torch.cuda.synchronize()
@@ -385,6 +398,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
     select_us = None
+    decode_only_us = None
     if args.eager:
         call_ms = np.array([[e0.elapsed_time(e1) for (e0, e1) in evs] for evs in step_evs])
         call_us = float(call_ms.mean() * 1e3)
@@ -397,6 +411,13 @@ def main():
         pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for _ in range(K)]
         for e0, e1 in pairs:
+            ulen_all.copy_(ulen0)  # the same append every launch
+            e0.record()
+            layer_graph.launch()
+            e1.record()
+        dpairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(K)]
+        for e0, e1 in dpairs:
             e0.record()
             decode_graph.launch()
             e1.record()
@@ -408,31 +429,48 @@ def main():
             e1.record()
         torch.cuda.synchronize()
         call_us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in pairs]) * 1e3 / n_layers)
+        decode_only_us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in dpairs]) * 1e3 / n_layers)
         select_us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in spairs]) * 1e3)
         step_graph.close()
+        layer_graph.close()
         decode_graph.close()
         select_graph.close()
 
     ms_per_step = ms_total / K
     value = w0.N_b * n_layers / (ms_per_step / 1e3)
-    t_hbm = alg["total"] / (PEAK_HBM_GBS * 1e9)
+    # The timed call is the fused append + decode when the layers append
+    # (one launch when the plan folds the append in): its bytes include the
+    # append's.
+    appends = layers[0][7] is not None
+    fused = appends and plan["mfma"] == 1 and plan["partials"] == 0
+    call_bytes = alg["total"] + (append_bytes(w0) if appends else 0)
+    t_hbm = call_bytes / (PEAK_HBM_GBS * 1e9)
     peak_tflops = PEAK_BF16_TFLOPS if w0.dtype == "bf16" else PEAK_FP32_TFLOPS
     t_mfma = alg["mfma_flops"] / (peak_tflops * 1e12)
     call_s = call_us * 1e-6
     if t_hbm >= t_mfma:
-        achieved = alg["total"] / call_s / 1e9
+        achieved = call_bytes / call_s / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBS, 4), traffic=measured_traffic(cfg))
     else:
         achieved = alg["mfma_flops"] / call_s / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=peak_tflops, unit="TFLOP/s",
                     frac=round(achieved / peak_tflops, 4), traffic=measured_traffic(cfg))
-    roof["kernel"] = "xattn_decode call (%d kernel launch%s)" % (plan["launches"], "" if plan["launches"] == 1 else "es")
-    roof["timing"] = ("HIP events around K launches of a graph of the n_layers decodes (interval / "
-                      "n_layers), run right after the timed steps" if not args.eager else
-                      "HIP events around every decode call of the timed steps")
+    if fused:
+        roof["kernel"] = "xattn_append_decode call (1 kernel launch: the append folded into the decode)"
+    elif appends:
+        roof["kernel"] = "xattn_append_decode call (append, then %d decode launch%s)" % (
+            plan["launches"], "" if plan["launches"] == 1 else "es")
+    else:
+        roof["kernel"] = "xattn_decode call (%d kernel launch%s)" % (plan["launches"], "" if plan["launches"] == 1 else "es")
+    roof["timing"] = ("HIP events around K launches of a graph of the n_layers calls (interval / "
+                      "n_layers; lengths restored before each launch, outside the events), run right "
+                      "after the timed steps" if not args.eager else
+                      "HIP events around every call of the timed steps")
     roof["avg_call_us"] = round(call_us, 3)
-    roof["algorithmic_bytes_per_call"] = alg["total"]
+    if decode_only_us is not None:
+        roof["decode_only_us"] = round(decode_only_us, 3)
+    roof["algorithmic_bytes_per_call"] = call_bytes
     roof["algorithmic_mfma_flops_per_call"] = alg["mfma_flops"]
     roof["kernel_hash"] = kernel_hash()
 
@@ -452,10 +490,10 @@ def main():
         "config": {"workload": WORKLOAD_NAMES[str(cfg)], "n_layers": n_layers,
                    "beams_per_call": w0.N_b,
                    "step": "beam selection (%d x %d x %d pool -> %d beams per request), then "
-                           "append + decode per layer" % (w0.R, w0.B, topk_k, w0.B),
+                           "append + decode per layer (one xattn_append_decode call)" % (w0.R, w0.B, topk_k, w0.B),
                    "launch": "eager" if args.eager else "graph", "plan": plan},
         "unique_kv_GBps": round(alg["unique_kv"] / call_s / 1e9, 1),
-        "total_GBps": round(alg["total"] / call_s / 1e9, 1),
+        "total_GBps": round(call_bytes / call_s / 1e9, 1),
         "mfma_TFLOPs": round(alg["mfma_flops"] / call_s / 1e12, 1),
         "wall_s_timed": round(wall, 4),
         "step_GBps": round(n_layers * (alg["total"] + append_bytes(w0)) / (ms_per_step * 1e-3) / 1e9, 1),
@@ -464,7 +502,7 @@ def main():
     }
     if not args.no_paged and w0.dtype == "bf16":
         print("timing the PagedAttention-style baseline ...", file=sys.stderr, flush=True)
-        result["paged_baseline"] = paged_baseline(layers, K, call_us, ms_per_step)
+        result["paged_baseline"] = paged_baseline(layers, K, decode_only_us or call_us, call_us, ms_per_step)
     result["batch_former"] = batch_former_timing()
     if not args.no_cpu_baseline:
         print("timing the oracle on host cores ...", file=sys.stderr, flush=True)

@@ -193,8 +193,25 @@ int launches(const xattn_dims* d, const Plan& p, int which) {
   return 2 + ((which == 2 && p.u_splits > 0) ? 1 : 0);
 }
 
+// Does xattn_append_decode fold the append into a single decode launch
+// under plan p? Its arrivals are counted per (request, kv head) over the row
+// tiles, then per request over the kv heads.
+bool append_folds(const xattn_dims* d, const Plan& p) {
+  return p.mfma && p.parts == 0 && d->max_unshared_len < (1 << kArrivalShift) &&
+         d->num_kv_heads <= kMaxAppendBlocks;
+}
+
+// which = 3 (xattn_append_decode): the arrival counters of a folded append,
+// else the decode's workspace.
 Layout layout_for(const xattn_dims* d, const Plan& p, int which) {
   Layout L{0, 0, 0, 0};
+  if (which == 3) {
+    if (append_folds(d, p)) {
+      L.total = align256((size_t)d->num_requests * d->num_kv_heads * sizeof(unsigned));
+      return L;
+    }
+    which = 2;
+  }
   const int64_t rows = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
   const int parts = p.parts;
   if (parts == 0) return L;
@@ -241,10 +258,23 @@ inline xattn_status hip_status(hipError_t e) { return e == hipSuccess ? XATTN_OK
 // Launch the prompt pass (MFMA or vector). `mode` selects how the MFMA kernel
 // writes (final / partial slot part_base+split / in-kernel split merge).
 // kp != null folds the Non-Shared tokens into prompt split 0.
+// The cache append folded into a single-launch decode (see xattn_append_decode).
+struct FusedAppend {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* parent;
+  const int64_t* slot_base;
+  const uint8_t* active;
+  void* k_pool;
+  void* v_pool;
+  int32_t* table_out;
+  int32_t* ulen;
+};
+
 hipError_t run_prefix(const xattn_dims* d, const Plan& p, int mode, const void* q, const void* ks,
                       const void* vs, const int64_t* poff, const int32_t* plen, const void* kp,
                       const void* vp, const int32_t* table, const int32_t* ulen, OutSpec out,
-                      const Workspace& w, hipStream_t st) {
+                      const Workspace& w, hipStream_t st, const FusedAppend* fa = nullptr) {
   const int64_t rows = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
   if (p.mfma) {
     SharedMfmaArgs a;
@@ -271,6 +301,17 @@ hipError_t run_prefix(const xattn_dims* d, const Plan& p, int mode, const void* 
     a.gen_member = (mode == kModeFixup && kp != nullptr) ? 1 : 0;
     a.stages = p.stages;
     a.key_groups = p.kgroups;
+    a.append = fa ? 1 : 0;
+    a.k_new = fa ? static_cast<const uint16_t*>(fa->k_new) : nullptr;
+    a.v_new = fa ? static_cast<const uint16_t*>(fa->v_new) : nullptr;
+    a.parent = fa ? fa->parent : nullptr;
+    a.slot_base = fa ? fa->slot_base : nullptr;
+    a.active = fa ? fa->active : nullptr;
+    a.k_pool_out = fa ? static_cast<uint16_t*>(fa->k_pool) : nullptr;
+    a.v_pool_out = fa ? static_cast<uint16_t*>(fa->v_pool) : nullptr;
+    a.table_out = fa ? fa->table_out : nullptr;
+    a.ulen_rw = fa ? fa->ulen : nullptr;
+    a.arrivals = d->num_kv_heads;  // per request, after each (request, kv head) has counted its row tiles
     return launch_shared_mfma(a, st);
   }
   ValuArgs a;
@@ -353,8 +394,8 @@ xattn_status xattn_get_plan(const xattn_dims* d, int which, xattn_plan* out) {
 xattn_status xattn_workspace_size(const xattn_dims* d, int which, size_t* bytes) {
   xattn_status e = check_dims(d);
   if (e != XATTN_OK) return e;
-  if (!bytes || which < 0 || which > 2) return XATTN_ERR_INVALID_ARG;
-  *bytes = ws_bytes_for(d, make_plan(d, which), which);
+  if (!bytes || which < 0 || which > 3) return XATTN_ERR_INVALID_ARG;
+  *bytes = ws_bytes_for(d, make_plan(d, which == 3 ? 2 : which), which);
   return XATTN_OK;
 }
 
@@ -488,6 +529,40 @@ xattn_status xattn_cache_append(const xattn_dims* d, const void* k_new, const vo
   a.unshared_len = ulen;
   if (!append_supported(a)) return XATTN_ERR_UNSUPPORTED;
   return hip_status(launch_append(a, static_cast<hipStream_t>(stream)));
+}
+
+xattn_status xattn_append_decode(const xattn_dims* d, const void* q, const void* ks, const void* vs,
+                                 const int64_t* poff, const int32_t* plen, const void* k_new,
+                                 const void* v_new, const int32_t* parent, const int64_t* slot_base,
+                                 const uint8_t* active, void* kp, void* vp, const int32_t* table_in,
+                                 int32_t* table_out, int32_t* ulen, float* o, float* lse, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  xattn_status e = check_dims(d);
+  if (e != XATTN_OK) return e;
+  if (!q || !poff || !plen || !k_new || !v_new || !parent || !slot_base || !kp || !vp || !table_in ||
+      !table_out || !ulen || !o)
+    return XATTN_ERR_INVALID_ARG;
+  if (table_in == table_out) return XATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(o) || !aligned16(k_new) || !aligned16(v_new) ||
+      !kv_ok(ks, vs, d->num_prefix_tokens) || !kv_ok(kp, vp, d->num_slots))
+    return XATTN_ERR_INVALID_ARG;
+  const int64_t N_b = (int64_t)d->num_requests * d->beam_width;
+  if (d->num_requests > 0 && d->num_slots < N_b) return XATTN_ERR_INVALID_ARG;
+  const Plan p = make_plan(d, 2);
+  const size_t need = ws_bytes_for(d, p, 3);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return XATTN_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!append_folds(d, p)) {
+    e = xattn_cache_append(d, k_new, v_new, parent, slot_base, active, kp, vp, table_in, table_out,
+                           ulen, stream);
+    if (e != XATTN_OK) return e;
+    return xattn_decode(d, q, ks, vs, poff, plen, kp, vp, table_out, ulen, o, lse, ws, ws_bytes, stream);
+  }
+  if (d->num_requests == 0) return XATTN_OK;
+  const FusedAppend fa{k_new, v_new, parent, slot_base, active, kp, vp, table_out, ulen};
+  const Workspace w{static_cast<unsigned*>(ws), nullptr, nullptr};
+  return hip_status(run_prefix(d, p, kModeFinal, q, ks, vs, poff, plen, kp, vp, table_in, ulen,
+                               OutSpec{o, lse, 0, 0}, w, st, &fa));
 }
 
 static size_t paged_ws_bytes(const xattn_dims* d, int32_t max_seq_len) {

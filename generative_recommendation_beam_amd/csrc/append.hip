@@ -53,11 +53,12 @@ AppendPlan plan_append(const AppendArgs& a) {
 
 // Arrive at request r's counter. Wave 0 makes the atomic while wave 1 reads
 // the request's activity flag and slot base, beside the workgroup's own
-// loads. Returns this call's position t to every thread (T_max, nothing to
-// write, for an inactive request or a full row) and the slot base; the last
-// of the request's nblk workgroups stores the new length.
+// loads. Returns this call's position t to every thread, whether the request
+// takes a new token (active, row not full), and the slot base; the last of
+// the request's nblk workgroups stores the new length.
 struct Arrival {
   int t;
+  bool grow;
   int64_t sbase;
 };
 __device__ __forceinline__ Arrival arrive(int32_t* ulen, const uint8_t* active, const int64_t* slot_base, int r,
@@ -74,7 +75,7 @@ __device__ __forceinline__ Arrival arrive(int32_t* ulen, const uint8_t* active, 
   const int t = old & ((1 << kArrivalShift) - 1);
   const bool grow = s_on != 0 && t < T_max;
   if (threadIdx.x == 0 && (old >> kArrivalShift) == nblk - 1) ulen[r] = grow ? t + 1 : t;
-  return Arrival{grow ? t : T_max, s_sb};
+  return Arrival{t, grow, s_sb};
 }
 
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, AppendPlan p) {
@@ -103,7 +104,17 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, Ap
     }
     const Arrival av = arrive(a.unshared_len, a.active, a.slot_base, r, nblk, a.T_max);
     const int t = av.t;
-    if (t >= a.T_max) return;
+    // A request that takes no token keeps its rows: copied into a separate
+    // table_out (nothing to do in place).
+    if (!av.grow) {
+      if (a.table_out == a.table_in) return;
+      int32_t* tout = a.table_out + nbase * a.T_max + c0;
+      for (int i = tid; i < cells; i += kAppendThreads) {
+        const int b = i / cw, c = i - b * cw;
+        if (c0 + c < t) tout[(int64_t)b * a.T_max + c] = tin[(int64_t)b * a.T_max + c];
+      }
+      return;
+    }
     if (c0 < t) {
 #pragma unroll
       for (int k = 0; k < kCells; ++k) {
@@ -152,7 +163,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a, Ap
   const uint4 v1 = *reinterpret_cast<const uint4*>(vn + min(i1, total - 1) * 16);
   const Arrival av = arrive(a.unshared_len, a.active, a.slot_base, r, nblk, a.T_max);
   const int t = av.t;
-  if (t >= a.T_max) return;
+  if (!av.grow) return;
   // Beam b's row goes to slot sb + b: piece i (beam i / pieces) keeps its
   // offset within the [B] block of rows.
   const int64_t sb = av.sbase + (int64_t)t * B;

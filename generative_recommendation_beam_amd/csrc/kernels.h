@@ -53,7 +53,24 @@ struct SharedMfmaArgs {
   int p_chunk;      // multiple of 64
   int gen_member;   // kModeFixup with k_pool: one extra member per group does the Non-Shared tokens
   int stages;       // LDS pipeline stages: 2 or 4
-  int key_groups;   // 1, or 2: waves/2 query rows per block, alternate 64-key tiles per half
+  int key_groups;   // 1, 2 or 4 wave groups splitting each workgroup's keys
+  // Fused cache append (kModeFinal, one member): slot_table is the table
+  // read (table_in), the new token of each active beam comes from
+  // k_new/v_new, and the launch also writes its pool rows, table_out and
+  // the new lengths, counting arrivals on unshared_len like the append.
+  int append;               // 0: plain decode
+  const uint16_t* k_new;    // [N_b][H_kv][D]
+  const uint16_t* v_new;
+  const int32_t* parent;    // [N_b]
+  const int64_t* slot_base; // [R]
+  const uint8_t* active;    // [R] or null
+  uint16_t* k_pool_out;     // = k_pool, written
+  uint16_t* v_pool_out;
+  int32_t* table_out;       // [N_b][T_max], not table_in
+  int32_t* ulen_rw;         // = unshared_len, counted and written
+  int arrivals;             // kv heads per request: second-level arrivals
+  // first-level arrivals: `counters` [R*H_kv], the row tiles of a (request,
+  // kv head), wrapping back to zero
 };
 hipError_t launch_shared_mfma(const SharedMfmaArgs& a, hipStream_t st);
 

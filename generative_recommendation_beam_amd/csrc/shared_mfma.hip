@@ -272,24 +272,31 @@ struct NonShared {
   static constexpr int NT = kMaxFusedTokens / KG;  // tokens per wave at most
   int L;  // generated tokens of the request (uniform)
   int kg;
-  const int32_t* trow;  // the beam's slot-table row
+  int tnew;  // fused append: index of the token read from knew/vnew, else -1
+  const int32_t* trow;  // the slot-table row the beam's tokens come from
   const uint16_t* kp;
   const uint16_t* vp;
+  const uint16_t* knew;  // this lane's parts of the beam's new K/V rows
+  const uint16_t* vnew;
   int hkv;
 
   // Does this wave take a u-th token (token kg + KG*u)?
   __device__ __forceinline__ bool has(int u) const { return kg + KG * u < L; }
-  __device__ __forceinline__ int slot(int u) const { return has(u) ? trow[kg + KG * u] : 0; }
+  __device__ __forceinline__ bool is_new(int u) const { return kg + KG * u == tnew; }
+  __device__ __forceinline__ int slot(int u) const { return has(u) && !is_new(u) ? trow[kg + KG * u] : 0; }
 
-  // This lane's parts of the K and V rows in pool slot `sl`.
-  __device__ __forceinline__ void fetch(int sl, uint4* kk, uint2 (*vv)[4]) const {
+  // This lane's parts of the K and V rows of token u (pool slot `sl`).
+  __device__ __forceinline__ void fetch(int u, int sl, uint4* kk, uint2 (*vv)[4]) const {
     const int64_t row = (int64_t)sl * hkv * D;
+    const bool nw = is_new(u);
+    const uint16_t* kr = nw ? knew : kp + row;
+    const uint16_t* vr = nw ? vnew : vp + row;
 #pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) kk[dc] = *reinterpret_cast<const uint4*>(kp + row + 16 * dc);
+    for (int dc = 0; dc < NDC; ++dc) kk[dc] = *reinterpret_cast<const uint4*>(kr + 16 * dc);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int ig = 0; ig < 4; ++ig) vv[db][ig] = *reinterpret_cast<const uint2*>(vp + row + 32 * db + 8 * ig);
+      for (int ig = 0; ig < 4; ++ig) vv[db][ig] = *reinterpret_cast<const uint2*>(vr + 32 * db + 8 * ig);
   }
 };
 
@@ -380,6 +387,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
                 "the key-group exchange must fit in the stage buffers");
   __shared__ __attribute__((aligned(1024))) char smem[NS * SBUF];
   __shared__ int s_last;
+  __shared__ int s_par[RG * 32 + 1];    // fused append: parents of the owned beams
 
   const int64_t lb64 = xcd_logical_block(blockIdx.x, gridDim.x, n_logical);
   if (lb64 < 0) return;  // uniform per workgroup
@@ -414,6 +422,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   // the one before it, the scalar cache returning out of order.
   // Rows past the last query row compute on a copy of that row (their
   // columns of S^T and O^T are independent of the others) and store nothing.
+  const bool app = a.append != 0;  // fused append (uniform)
   const int row = tile * (RG * 32) + rg * 32 + ql;
   const bool row_ok = row < M;
   const int rowc = min(row, M - 1);
@@ -423,6 +432,9 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   // Non-Shared tokens: in the generated-token member, or (no such member) in
   // prompt split 0. They are folded in after the prompt tiles.
   const bool do_ns = a.k_pool != nullptr && (gen_only || (!a.gen_member && member == 0));
+  // Slot cells read now come from this beam's row; with the fused append
+  // they depend on the parent and are read once it is known.
+  const bool early_slots = do_ns && !app;
   // With one workgroup per CU and registers to spare, the first NPF tokens'
   // K/V rows are requested right after the first super-tile's compute, so
   // they have landed by the end of the loop; the others are fetched after
@@ -438,12 +450,21 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   // prefix_len[0], which always exists; slot cells are clamped to the row
   // and ignored beyond the length.
   const int32_t* lenp = do_ns ? a.unshared_len + r : a.prefix_len;
-  const int32_t* trow = do_ns ? a.slot_table + ((int64_t)r * s.B + bq) * s.T_max : a.prefix_len;
-  const int tlast = do_ns ? s.T_max - 1 : 0;
+  const int32_t* trow = early_slots ? a.slot_table + ((int64_t)r * s.B + bq) * s.T_max : a.prefix_len;
+  const int tlast = early_slots ? s.T_max - 1 : 0;
   const int lenv = lenp[zv];
   int pslot[NSL];
 #pragma unroll
   for (int u = 0; u < NSL; ++u) pslot[u] = trow[min(kg + KG * u, tlast)];
+  // Fused append: the request's activity flag, the row's parent and the
+  // request's slot base (valid stand-in addresses otherwise).
+  const bool has_act = app && a.active != nullptr;
+  const uint8_t* actp = has_act ? a.active + r : reinterpret_cast<const uint8_t*>(a.prefix_len);
+  const int32_t* parp = app ? a.parent + (int64_t)r * s.B + bq : a.prefix_len;
+  const int64_t* sbp = app ? a.slot_base + r : a.prefix_off;
+  const int actv = actp[zv];
+  const int parv = parp[zv];
+  const int64_t sbv = sbp[zv];
   bf16x8_t qf[NDC];
   {
     const uint16_t* qp = a.q + qrow * D + 8 * hh;
@@ -490,11 +511,14 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
     }
   };
   NonShared<D, KG> ns;
-  ns.L = do_ns ? __builtin_amdgcn_readfirstlane(lenv) : 0;
+  ns.L = early_slots ? __builtin_amdgcn_readfirstlane(lenv) : 0;  // the fused append sets it below
   ns.kg = kg;
+  ns.tnew = -1;
   ns.hkv = s.Hkv;
   ns.kp = do_ns ? a.k_pool + (int64_t)h * D + 8 * hh : a.q;
   ns.vp = do_ns ? a.v_pool + (int64_t)h * D + 4 * hh : a.q;
+  ns.knew = ns.kp;
+  ns.vnew = ns.vp;
   ns.trow = trow;
   uint4 pk[NPF > 0 ? NPF : 1][NDC];
   uint2 pv[NPF > 0 ? NPF : 1][NDB][4];
@@ -504,7 +528,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
 #pragma unroll
     for (int u = 0; u < NPF; ++u) {
       const int sl = ns.has(u) ? pslot[u] : 0;
-      ns.fetch(sl, pk[u], pv[u]);
+      ns.fetch(u, sl, pk[u], pv[u]);
     }
   };
 
@@ -516,6 +540,45 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
       issue_tile(t);
       issued = t + 1;
     }
+  }
+
+  // Fused append. This workgroup owns the beams whose first query row is in
+  // its row tile: it copies their new K/V rows (head h) to the pool and, at
+  // head 0, writes their table_out rows. t comes from the length read above
+  // (its low bits: other workgroups' arrivals only touch the bits from
+  // kArrivalShift up); the workgroup arrives after its prompt loop (where
+  // the workgroups of a request arrive spread out in time: same-address
+  // atomics are serialized, and the round trip overlaps the token fetches),
+  // and the request's last arrival, necessarily after every workgroup's
+  // read, stores the new length at its end. The beam's tokens come from the
+  // parent's row of table_in plus the new row for an active request with
+  // room, else its own row.
+  const int RPB = RG * 32;  // query rows per workgroup
+  const int b_lo = (tile * RPB + G - 1) / G;
+  const int nb_own = max(0, min(s.B, (tile * RPB + RPB + G - 1) / G) - b_lo);
+  int t_app = 0;
+  bool grow = false;
+  int old_arr = 0;  // this workgroup's arrival (thread 0)
+  uint4 cpv = make_uint4(0, 0, 0, 0);  // this thread's first K/V chunk to copy
+  if (app) {  // uniform; always member 0 with Non-Shared tokens
+    if (kg == 0 && row_ok && gq == 0) s_par[bq - b_lo] = parv;  // read after the next barrier
+    t_app = __builtin_amdgcn_readfirstlane(lenv) & ((1 << kArrivalShift) - 1);
+    grow = __builtin_amdgcn_readfirstlane(actv) != 0 && t_app < s.T_max;
+    ns.L = grow ? t_app + 1 : t_app;
+    ns.tnew = grow ? t_app : -1;
+    ns.trow = a.slot_table + ((int64_t)r * s.B + (grow ? parv : bq)) * s.T_max;
+    // The first pass of the K/V copy: its source does not depend on t, so it
+    // is requested now and stored right after the prompt loop.
+    if (grow && tid < nb_own * 2 * (D / 8)) {
+      const int bl = tid / (D / 4), pc = tid - bl * (D / 4);
+      cpv = *reinterpret_cast<const uint4*>((pc < D / 8 ? a.k_new : a.v_new) +
+                                            (((int64_t)r * s.B + b_lo + bl) * s.Hkv + h) * D + 8 * (pc % (D / 8)));
+    }
+    const int64_t nrow = (((int64_t)r * s.B + bq) * s.Hkv + h) * D;
+    ns.knew = a.k_new + nrow + 8 * hh;
+    ns.vnew = a.v_new + nrow + 4 * hh;
+#pragma unroll
+    for (int u = 0; u < NSL; ++u) pslot[u] = ns.slot(u);
   }
 
 
@@ -601,6 +664,53 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
 
   wait_vmem();  // every tile load has landed before the stage buffers are reused
 
+  // Fused append writes: the first K/V chunk (loaded in the prologue) is
+  // stored now; the first table cells are requested before the tokens' rows
+  // (one round trip for both) and stored after them; further passes follow.
+  constexpr int NTH = NW * 64;
+  constexpr int CH = D / 8;                      // 16-byte chunks per K (or V) row
+  const int n_cp = grow ? nb_own * 2 * CH : 0;   // K/V chunks to copy
+  const int tc = grow ? t_app + 1 : t_app;       // table cells per owned row
+  const int n_tb = (app && h == 0) ? nb_own * tc : 0;
+  const int64_t sb_new = sbv + (int64_t)t_app * s.B;  // slot of beam 0's new row
+  auto cp_src = [&](int i) {
+    const int bl = i / (2 * CH), pc = i - bl * (2 * CH);
+    const uint16_t* base = pc < CH ? a.k_new : a.v_new;
+    return reinterpret_cast<const uint4*>(base + (((int64_t)r * s.B + b_lo + bl) * s.Hkv + h) * D + 8 * (pc % CH));
+  };
+  auto cp_dst = [&](int i) {
+    const int bl = i / (2 * CH), pc = i - bl * (2 * CH);
+    uint16_t* base = pc < CH ? a.k_pool_out : a.v_pool_out;
+    return reinterpret_cast<uint4*>(base + ((sb_new + b_lo + bl) * s.Hkv + h) * D + 8 * (pc % CH));
+  };
+  auto tb_val = [&](int i) {  // table_out cell i of the owned rows
+    const int bl = i / tc, j = i - bl * tc;
+    if (j == t_app) return (int32_t)(sb_new + b_lo + bl);
+    const int src = grow ? s_par[bl] : b_lo + bl;
+    return a.slot_table[((int64_t)r * s.B + src) * s.T_max + j];
+  };
+  auto tb_dst = [&](int i) {
+    const int bl = i / tc, j = i - bl * tc;
+    return a.table_out + ((int64_t)r * s.B + b_lo + bl) * s.T_max + j;
+  };
+  int32_t tbv = 0;
+  if (app) {  // uniform
+    if (tid < n_cp) *cp_dst(tid) = cpv;
+    if (tid == 0) {
+      // Two-level arrival (same-address atomics serialize): the row tiles of
+      // (request, kv head) count on its own counter, which wraps back to zero;
+      // the last of them arrives for the pair on the request's length.
+      const unsigned n1 = __builtin_amdgcn_atomic_inc32(a.counters + pair, (unsigned)(a.row_tiles - 1),
+                                                        __ATOMIC_RELAXED, "agent");
+      if (n1 == (unsigned)(a.row_tiles - 1))
+        old_arr = atomicAdd(a.ulen_rw + r, 1 << kArrivalShift);
+      else
+        old_arr = -1;  // not the pair's last
+    }
+    if (nsup == 0) __syncthreads();  // no loop barrier since the parents went to LDS
+    if (tid < n_tb) tbv = tb_val(tid);
+  }
+
   // The Non-Shared tokens: prefetched ones first, then the rest one at a time
   // with the next slot index in flight beside each token's K/V rows.
 #pragma unroll
@@ -611,10 +721,18 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
     for (int u = NPF; u < NonShared<D, KG>::NT && ns.has(u); ++u) {
       uint4 kk[NDC];
       uint2 vv[NDB][4];
-      ns.fetch(sl, kk, vv);
+      ns.fetch(u, sl, kk, vv);
       sl = ns.slot(u + 1);
       token_update<D>(kk, vv, qf, oacc, m_run, l_part, c, hh);
     }
+  }
+
+  if (app) {  // uniform
+    if (tid < n_tb) *tb_dst(tid) = tbv;
+    for (int i = tid + NTH; i < n_cp; i += NTH) *cp_dst(i) = *cp_src(i);
+    for (int i = tid + NTH; i < n_tb; i += NTH) *tb_dst(i) = tb_val(i);
+    if (tid == 0 && old_arr >= 0 && (old_arr >> kArrivalShift) == a.arrivals - 1)
+      a.ulen_rw[r] = grow ? t_app + 1 : t_app;
   }
 
   float l_tot = l_part + __shfl_xor(l_part, 32);

@@ -28,18 +28,26 @@ xattn_status capture_step(const xattn_beam_select* sel, const xattn_layer_step* 
   for (int i = 0; i < n; ++i) {
     const xattn_layer_step& l = layers[i];
     xattn_status e;
-    if (l.k_new != nullptr) {
-      e = xattn_cache_append(&l.dims, l.k_new, l.v_new, l.parent, l.slot_base, l.active, l.k_pool,
-                             l.v_pool, l.table_in, l.table_out, l.unshared_len, cs);
+    if (l.k_new != nullptr && l.table_in != l.table_out && l.decode_begin == nullptr) {
+      // Ping-pong tables: the append folds into the decode launch when the plan allows.
+      e = xattn_append_decode(&l.dims, l.q, l.k_shared, l.v_shared, l.prefix_off, l.prefix_len, l.k_new,
+                              l.v_new, l.parent, l.slot_base, l.active, l.k_pool, l.v_pool, l.table_in,
+                              l.table_out, l.unshared_len, l.o, l.lse, l.workspace, l.workspace_bytes, cs);
+      if (e != XATTN_OK) return e;
+    } else {
+      if (l.k_new != nullptr) {
+        e = xattn_cache_append(&l.dims, l.k_new, l.v_new, l.parent, l.slot_base, l.active, l.k_pool,
+                               l.v_pool, l.table_in, l.table_out, l.unshared_len, cs);
+        if (e != XATTN_OK) return e;
+      }
+      if (l.decode_begin && hipEventRecordWithFlags(static_cast<hipEvent_t>(l.decode_begin), cs,
+                                                    hipEventRecordExternal) != hipSuccess)
+        return XATTN_ERR_HIP;
+      e = xattn_decode(&l.dims, l.q, l.k_shared, l.v_shared, l.prefix_off, l.prefix_len, l.k_pool,
+                       l.v_pool, l.table_out, l.unshared_len, l.o, l.lse, l.workspace,
+                       l.workspace_bytes, cs);
       if (e != XATTN_OK) return e;
     }
-    if (l.decode_begin && hipEventRecordWithFlags(static_cast<hipEvent_t>(l.decode_begin), cs,
-                                                  hipEventRecordExternal) != hipSuccess)
-      return XATTN_ERR_HIP;
-    e = xattn_decode(&l.dims, l.q, l.k_shared, l.v_shared, l.prefix_off, l.prefix_len, l.k_pool,
-                     l.v_pool, l.table_out, l.unshared_len, l.o, l.lse, l.workspace,
-                     l.workspace_bytes, cs);
-    if (e != XATTN_OK) return e;
     if (l.decode_end && hipEventRecordWithFlags(static_cast<hipEvent_t>(l.decode_end), cs,
                                                 hipEventRecordExternal) != hipSuccess)
       return XATTN_ERR_HIP;

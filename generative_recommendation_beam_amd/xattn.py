@@ -20,7 +20,7 @@ XATTN_OK, XATTN_ERR_INVALID_ARG, XATTN_ERR_UNSUPPORTED, XATTN_ERR_WORKSPACE, XAT
 XATTN_F32, XATTN_BF16 = 0, 1
 
 EXPORTED = ("xattn_workspace_size", "xattn_get_plan", "xattn_shared_stage", "xattn_unshared_stage",
-            "xattn_merge", "xattn_decode", "xattn_cache_append", "xattn_beam_topk",
+            "xattn_merge", "xattn_decode", "xattn_cache_append", "xattn_append_decode", "xattn_beam_topk",
             "xattn_paged_workspace_size", "xattn_paged_decode", "xattn_paged_copy_blocks",
             "xattn_cht_create", "xattn_cht_destroy", "xattn_cht_insert", "xattn_cht_best",
             "xattn_cht_admit", "xattn_cht_complete", "xattn_cht_form_batch", "xattn_step_graph_create",
@@ -108,6 +108,8 @@ def lib():
     L.xattn_decode.argtypes = [pd, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     L.xattn_cache_append.restype = ctypes.c_int
     L.xattn_cache_append.argtypes = [pd, P, P, P, P, P, P, P, P, P, P, P]
+    L.xattn_append_decode.restype = ctypes.c_int
+    L.xattn_append_decode.argtypes = [pd] + [P] * 18 + [ctypes.c_size_t, P]
     L.xattn_paged_workspace_size.restype = ctypes.c_int
     L.xattn_paged_workspace_size.argtypes = [pd, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     L.xattn_paged_decode.restype = ctypes.c_int
@@ -229,6 +231,18 @@ def cache_append(dims, k_new, v_new, parent, slot_base, active, k_pool, v_pool, 
                                     _ptr(table_in), _ptr(table_out), _ptr(unshared_len),
                                     _stream(stream)),
            "xattn_cache_append")
+
+
+def append_decode(dims, q, k_shared, v_shared, prefix_off, prefix_len, k_new, v_new, parent, slot_base,
+                  active, k_pool, v_pool, table_in, table_out, unshared_len, o, lse=None, workspace=None,
+                  workspace_bytes=0, stream=None):
+    _check(lib().xattn_append_decode(ctypes.byref(dims), _ptr(q), _ptr(k_shared), _ptr(v_shared),
+                                     _ptr(prefix_off), _ptr(prefix_len), _ptr(k_new), _ptr(v_new),
+                                     _ptr(parent), _ptr(slot_base), _ptr(active), _ptr(k_pool),
+                                     _ptr(v_pool), _ptr(table_in), _ptr(table_out), _ptr(unshared_len),
+                                     _ptr(o), _ptr(lse), _ptr(workspace), int(workspace_bytes),
+                                     _stream(stream)),
+           "xattn_append_decode")
 
 
 def paged_workspace_size(dims, max_seq_len) -> int:

@@ -116,8 +116,9 @@ typedef struct {
 
 /*
  * Workspace bytes needed by a call. which: 0 = xattn_shared_stage,
- * 1 = xattn_unshared_stage, 2 = xattn_decode. A size of 0 means the call needs
- * no workspace (a null workspace pointer is then allowed).
+ * 1 = xattn_unshared_stage, 2 = xattn_decode, 3 = xattn_append_decode. A
+ * size of 0 means the call needs no workspace (a null workspace pointer is
+ * then allowed).
  * The workspace (device memory, 16-byte aligned, owned by the caller) starts
  * with a block of split counters that must be zero-filled before the buffer's
  * first use; every call returns them to zero, so a buffer is reusable by any
@@ -199,8 +200,10 @@ xattn_status xattn_decode(const xattn_dims* dims, const void* q, const void* k_s
  * k_new / v_new: [N_b][H_kv][D] (dims.dtype); parent [N_b] int32;
  * slot_base [R] int64; active [R] uint8 or NULL; tables [N_b][T_max] int32;
  * unshared_len [R] int32 (read, then incremented). Needs no workspace.
- * Slots must lie in [0, num_slots). A request whose row is full
- * (t == max_unshared_len) is left unchanged.
+ * Slots must lie in [0, num_slots). A request that takes no token (inactive,
+ * or its row full: t == max_unshared_len) keeps its length and pool; with a
+ * separate table_out its rows are copied there (columns 0..t-1), so that
+ * table_out is a complete table either way.
  * One kernel launch: while it runs, its workgroups count their arrivals in
  * bits 20 and up of unshared_len, so lengths must stay below 2^20 and nothing
  * else may read unshared_len during the call. XATTN_ERR_UNSUPPORTED if
@@ -212,6 +215,34 @@ xattn_status xattn_cache_append(const xattn_dims* dims, const void* k_new, const
                                 const uint8_t* active, void* k_pool, void* v_pool,
                                 const int32_t* table_in, int32_t* table_out,
                                 int32_t* unshared_len, void* stream);
+
+/*
+ * One decode step of a layer in one call: xattn_cache_append of the step's
+ * new K/V rows, then xattn_decode over the updated cache (xGR page, section
+ * 2.1: the token-granular in-place update and the staged attention of the
+ * same step). Arguments are those of the two calls; the decode reads
+ * table_out, which must be a different buffer from table_in (the ping-pong
+ * form: the next step passes this table_out as its table_in). The result is
+ * bit for bit that of the two calls in order.
+ * When the decode plan is a single launch (bf16 MFMA path, one prompt range,
+ * Non-Shared tokens folded in) the append is folded into that launch: each
+ * attention workgroup counts its arrival on unshared_len as the append does,
+ * reads every beam's older tokens through its parent's row of table_in and
+ * its new token straight from k_new / v_new, and writes the pool rows,
+ * table_out rows and lengths of the beams it owns; arrivals are counted per
+ * (request, kv head) in the workspace (which = 3 in xattn_workspace_size),
+ * then per request on unshared_len. Otherwise the two calls are made in
+ * order, with the decode's workspace. Same limits and errors as the two
+ * calls, and XATTN_ERR_INVALID_ARG if table_out == table_in.
+ */
+xattn_status xattn_append_decode(const xattn_dims* dims, const void* q, const void* k_shared,
+                                 const void* v_shared, const int64_t* prefix_off,
+                                 const int32_t* prefix_len, const void* k_new, const void* v_new,
+                                 const int32_t* parent, const int64_t* slot_base,
+                                 const uint8_t* active, void* k_pool, void* v_pool,
+                                 const int32_t* table_in, int32_t* table_out,
+                                 int32_t* unshared_len, float* o, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /*
  * Beam-search survivor selection for one decode step (xGR page, section 2.2
@@ -283,7 +314,9 @@ xattn_status xattn_paged_copy_blocks(const xattn_dims* dims, void* k_cache, void
  * normally read), then, for every layer in order, xattn_cache_append
  * (skipped when k_new is NULL) and xattn_decode on the table the append
  * wrote (table_out), with the arguments below exactly as those calls take
- * them.
+ * them. With separate tables (table_in != table_out) and no decode_begin
+ * event, the pair is captured as one xattn_append_decode call, which folds
+ * the append into the decode launch where the plan allows.
  * Positions are read from device memory when the graph runs, so one graph
  * serves every decode step: refill the candidates, q, k_new and v_new in
  * place and launch it again. If decode_begin / decode_end are not NULL (hipEvent_t

@@ -94,6 +94,18 @@ def test_workspace_too_small_rejected(L):
     assert _decode(d, ws=FAKE, nbytes=need - 1) == xattn.XATTN_ERR_WORKSPACE
 
 
+def test_workspace_size_for_append_decode(L):
+    """which = 3: the folded append needs only its per-(request, kv head)
+    arrival counters; a plan that cannot fold needs the decode's workspace."""
+    d = dims(R=8, B=128, Hq=16, Hkv=4, max_prefix_len=1024, max_unshared_len=3)
+    assert xattn.get_plan(d, 2)["partials"] == 0
+    assert xattn.workspace_size(d, 3) == 256  # 8 x 4 counters, 256-byte aligned
+    d2 = dims(R=2, B=12, Hq=8, Hkv=2, max_prefix_len=640, max_unshared_len=3, prefix_splits=3)
+    assert xattn.workspace_size(d2, 3) == xattn.workspace_size(d2, 2) > 0
+    n = ctypes.c_size_t(0)
+    assert L.xattn_workspace_size(ctypes.byref(d), 4, ctypes.byref(n)) == xattn.XATTN_ERR_INVALID_ARG
+
+
 def test_plan_introspection(L):
     d = dims(R=8, B=128, Hq=16, Hkv=4, max_prefix_len=1024, max_unshared_len=3)
     p = xattn.get_plan(d, 2)

@@ -61,7 +61,7 @@ def test_step_graph_every_replay_matches_oracle():
         w = make_workload(f"step{i}", seed_key=(320, i), **kw)
         d = dv.upload(w)
         table_in, table_out, t_last = dv.prepare_step(d)
-        o, lse, ws, nb = dv.alloc_outputs(d, 2)
+        o, lse, ws, nb = dv.alloc_outputs(d, 3)
         steps.append(dv.layer_step(d, o, lse, ws, nb, table_in, table_out, t_last))
         ws_.append(w)
         ds.append((d, table_out))
@@ -96,7 +96,7 @@ def test_step_graph_equals_eager_bitwise():
     d = dv.upload(w)
     table_in, table_out, t_last = dv.prepare_step(d)
     u0 = d.unshared_len.clone()
-    o, lse, ws, nb = dv.alloc_outputs(d, 2)
+    o, lse, ws, nb = dv.alloc_outputs(d, 3)
     g = xattn.StepGraph([dv.layer_step(d, o, lse, ws, nb, table_in, table_out, t_last)])
     try:
         g.launch()
@@ -116,7 +116,7 @@ def test_step_graph_rejects_bad_layer_without_keeping_anything():
     w = make_workload("stepBad", seed_key=(322, 0), **LAYERS[0])
     d = dv.upload(w)
     table_in, table_out, t_last = dv.prepare_step(d)
-    o, lse, ws, nb = dv.alloc_outputs(d, 2)
+    o, lse, ws, nb = dv.alloc_outputs(d, 3)
     good = dv.layer_step(d, o, lse, ws, nb, table_in, table_out, t_last)
     bad = dv.layer_step(d, o, lse, ws, nb, table_in, table_out, t_last)
     bad.q = None
@@ -174,7 +174,7 @@ def test_step_graph_with_selection_feeds_every_layer():
         w = make_workload(f"sel{i}", seed_key=(325, i), **kw)
         d = dv.upload(w)
         table_in, table_out, t_last = dv.prepare_step(d)
-        o, lse, ws, nb = dv.alloc_outputs(d, 2)
+        o, lse, ws, nb = dv.alloc_outputs(d, 3)
         st = dv.layer_step(d, o, lse, ws, nb, table_in, table_out, t_last)
         st.parent = parent.data_ptr()   # the appends read the selection's output
         steps.append(st)
