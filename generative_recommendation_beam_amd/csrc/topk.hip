@@ -81,6 +81,62 @@ __device__ __forceinline__ void store_regs(const uint64_t* v, uint64_t* keys, in
   }
 }
 
+// Bitonic sort of 64 * S keys held by one wavefront, S per lane (element
+// e = S * lane + s), into descending order: strides below S swap inside a
+// lane, larger ones pair lanes through shuffles. No barrier and no LDS, which
+// for a few hundred keys beats the workgroup sort's barrier-bound stages.
+template <int S>
+__device__ __forceinline__ void wave_sort_desc(uint64_t* v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 64 * S; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride >= 1; stride >>= 1) {
+      if (stride < S) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          if (s & stride) continue;
+          const int e = S * lane + s;
+          const bool desc = (e & size) == 0;
+          const uint64_t a = v[s], b = v[s + stride];
+          const bool swap = desc ? a < b : a > b;
+          v[s] = swap ? b : a;
+          v[s + stride] = swap ? a : b;
+        }
+      } else {
+        const int lm = stride / S;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const int e = S * lane + s;
+          const uint64_t p = __shfl_xor(v[s], lm);
+          const bool keep_max = ((e & size) == 0) == ((e & stride) == 0);
+          v[s] = keep_max ? (v[s] > p ? v[s] : p) : (v[s] < p ? v[s] : p);
+        }
+      }
+    }
+  }
+}
+
+// The n (<= 64 * S) keys of keys_in[] (or computed by key_of(i)) sorted by
+// wave 0; the first n_keep land in out[] in order. Other waves do nothing.
+template <int S, typename F>
+__device__ __forceinline__ void wave_sort_to(F&& key_of, int n, uint64_t* out, int n_keep) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  uint64_t v[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int e = S * lane + s;
+    v[s] = e < n ? key_of(e) : 0ull;
+  }
+  wave_sort_desc<S>(v);
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int e = S * lane + s;
+    if (e < n_keep) out[e] = v[s];
+  }
+}
+
 // Caller: keys[0, n) written and visible (a barrier since). Ends with a
 // barrier, the sorted keys in LDS.
 __device__ void sort_desc(uint64_t* keys, int n) {
@@ -114,7 +170,7 @@ __device__ void sort_desc(uint64_t* keys, int n) {
 
 __global__ __launch_bounds__(kThreads) void beam_topk_kernel(TopkArgs a) {
   __shared__ uint64_t keys[kTopkCap];
-  __shared__ int act[2][kTopkMaxBeams];  // beams still walking, per round parity
+  __shared__ __attribute__((aligned(16))) int act[2][kTopkMaxBeams];  // beams still walking, per round parity
   __shared__ int s_count, s_nact[2];
   const int r = blockIdx.x;
   const int BW = a.BW, K = a.K, N = a.n_out;
@@ -130,17 +186,21 @@ __global__ __launch_bounds__(kThreads) void beam_topk_kernel(TopkArgs a) {
   m = max(1, min(m, min(K, kTopkCap / BW)));
   const int n_s = BW * m;
   if (n_s >= N) {
-    const int n2 = next_pow2(n_s);
-    for (int i = tid; i < n2; i += kThreads) {
-      uint64_t key = 0ull;
-      if (i < n_s) {
-        const int b = i / m, k = i - (i / m) * m;
-        key = make_key(bs[b] + lp[(int64_t)b * K + k], (uint32_t)b * (uint32_t)K + (uint32_t)k);
-      }
-      keys[i] = key;
+    auto sample = [&](int i) {
+      const int b = i / m, k = i - (i / m) * m;
+      return make_key(bs[b] + lp[(int64_t)b * K + k], (uint32_t)b * (uint32_t)K + (uint32_t)k);
+    };
+    if (n_s <= 512) {
+      wave_sort_to<8>(sample, n_s, keys, N);
+    } else if (n_s <= 1024) {
+      wave_sort_to<16>(sample, n_s, keys, N);
+    } else {
+      const int n2 = next_pow2(n_s);
+      for (int i = tid; i < n2; i += kThreads) keys[i] = i < n_s ? sample(i) : 0ull;
+      __syncthreads();
+      sort_desc(keys, n2);
     }
     __syncthreads();
-    sort_desc(keys, n2);
     tau = keys[N - 1];
     __syncthreads();
   }
@@ -209,10 +269,24 @@ __global__ __launch_bounds__(kThreads) void beam_topk_kernel(TopkArgs a) {
   if (!overflow) {
     // 3. Sort the survivors; the n_out largest lead.
     const int n = n_found;
-    const int n2 = next_pow2(n);
-    for (int i = n + tid; i < n2; i += kThreads) keys[i] = 0ull;
-    __syncthreads();
-    sort_desc(keys, n2);
+    if (n <= 1024) {
+      // One wave sorts them in registers into the other buffer (act, free
+      // after the walk).
+      uint64_t* sorted = reinterpret_cast<uint64_t*>(&act[0][0]);
+      auto survivor = [&](int i) { return keys[i]; };
+      if (n <= 512)
+        wave_sort_to<8>(survivor, n, sorted, N);
+      else
+        wave_sort_to<16>(survivor, n, sorted, N);
+      __syncthreads();
+      for (int i = tid; i < N; i += kThreads) keys[i] = sorted[i];
+      __syncthreads();
+    } else {
+      const int n2 = next_pow2(n);
+      for (int i = n + tid; i < n2; i += kThreads) keys[i] = 0ull;
+      __syncthreads();
+      sort_desc(keys, n2);
+    }
     n_top = N;
   } else {
     // Exact fallback: merge blocks of whole beams into a running best set
