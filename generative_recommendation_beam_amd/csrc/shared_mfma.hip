@@ -173,13 +173,20 @@ __device__ __forceinline__ void half_softmax_pv(const char* buf, int vbase, f32x
     }
 }
 
+// Does nothing: the hook of a step that starts no loads.
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+
 // One 64-key tile for one wavefront (32 query rows): S^T = K.Q^T on MFMA for
 // both 32-key halves, then per half the online softmax and O^T += V^T.P^T.
 // MASK: the tile holds only `nvalid` keys (the last tile of a range).
-template <int D, bool MASK>
+// after_s() runs once the S^T MFMAs are issued (the loop starts the next
+// tile's V loads there).
+template <int D, bool MASK, typename F = NoHook>
 __device__ __forceinline__ void tile_step(const char* buf, int kbase, int vbase, const bf16x8_t* qf,
                                           f32x16_t* oacc, float& m_run, float& l_part, float c,
-                                          int hh, int nvalid) {
+                                          int hh, int nvalid, F&& after_s = F()) {
   using TG = TileGeom<D>;
   constexpr int NDC = D / 16;
   f32x16_t sacc[2];
@@ -203,6 +210,7 @@ __device__ __forceinline__ void tile_step(const char* buf, int kbase, int vbase,
     for (int kb = 0; kb < 2; ++kb)
       sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc][kb], qf[dc], sacc[kb], 0, 0, 0);
   __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDC, 0);  // then the MFMAs
+  after_s();
   half_softmax_pv<D, MASK>(buf, vbase, sacc[0], 0, oacc, m_run, l_part, c, hh, nvalid);
   half_softmax_pv<D, MASK>(buf, vbase, sacc[1], 1, oacc, m_run, l_part, c, hh, nvalid);
 }
@@ -210,10 +218,10 @@ __device__ __forceinline__ void tile_step(const char* buf, int kbase, int vbase,
 // One 32-key half (kb) of a 64-key tile for one wavefront: the S^T MFMAs of
 // that half, its online softmax and its P.V MFMAs (two key groups splitting
 // each tile between them).
-template <int D, bool MASK>
+template <int D, bool MASK, typename F = NoHook>
 __device__ __forceinline__ void half_tile_step(const char* buf, int kbase, int vbase, const bf16x8_t* qf,
                                                f32x16_t* oacc, float& m_run, float& l_part, float c, int hh,
-                                               int nvalid, int kb) {
+                                               int nvalid, int kb, F&& after_s = F()) {
   using TG = TileGeom<D>;
   constexpr int NDC = D / 16;
   f32x16_t sacc;
@@ -227,6 +235,7 @@ __device__ __forceinline__ void half_tile_step(const char* buf, int kbase, int v
 #pragma unroll
   for (int dc = 0; dc < NDC; ++dc) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc], qf[dc], sacc, 0, 0, 0);
   __builtin_amdgcn_sched_group_barrier(0x008, NDC, 0);
+  after_s();
   half_softmax_pv<D, MASK>(buf, vbase, sacc, kb, oacc, m_run, l_part, c, hh, nvalid);
 }
 
@@ -500,16 +509,18 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   // the workgroup that started there. The last (possibly partial) super-tile
   // stays last. The softmax result does not depend on the order.
   const int rot = (KG >= 2 && nsup > 2) ? tile % (nsup - 1) : 0;
-  auto issue_tile = [&](int t) {
+  auto issue_part = [&](int t, bool do_k, bool do_v) {
     lds_char* buf = lsm + (t % NS) * SBUF + wave * 1024;
     const int pt = t < nsup - 1 ? (t + rot) % (nsup - 1) : t;  // super-tile loaded at step t
     const uint32_t tile_bytes = (uint32_t)((kbeg + pt * ST) * TG::ROWB);
 #pragma unroll
     for (int j = 0; j < LP::NJ; ++j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, buf + LP::lds_off(j), 16, lp.k[j], tile_bytes, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, buf + LP::lds_off(j) + TG::TILEB, 16, lp.v[j], tile_bytes, 0, 0);
+      if (do_k) __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, buf + LP::lds_off(j), 16, lp.k[j], tile_bytes, 0, 0);
+      if (do_v)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, buf + LP::lds_off(j) + TG::TILEB, 16, lp.v[j], tile_bytes, 0, 0);
     }
   };
+  auto issue_tile = [&](int t) { issue_part(t, true, true); };
   NonShared<D, KG> ns;
   ns.L = early_slots ? __builtin_amdgcn_readfirstlane(lenv) : 0;  // the fused append sets it below
   ns.kg = kg;
@@ -616,6 +627,11 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   // super-tile tok_after; whatever was issued after super-tile `it` may stay
   // in flight.
   int tok_after = -1;
+  // Half-tile steps with two stages (one workgroup per CU) split the refill:
+  // its K tiles go out here and its V tiles once the step's S^T MFMAs are
+  // issued (v_pending), which spreads the LDS writes over the step. Measured
+  // on MI355X: faster there, slower where two workgroups share a CU.
+  int v_pending = -1;
   auto advance = [&](int it) {
     if (NPF > 0 && NS == 2 && it == 1)  // the token rows requested after tile 1's loads may stay in flight
       __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(NPF * (NDC + 4 * NDB)) : "memory");
@@ -624,20 +640,29 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
     else
       wait_tiles<LPT>(min(issued - 1 - it, NS - 2));
     __syncthreads();  // super-tile `it` landed for every wave; it-1's buffer is free
+    v_pending = -1;
     if (issued < nsup) {
-      issue_tile(issued);
+      if constexpr (NS == 2 && HALF) {
+        issue_part(issued, true, false);
+        v_pending = issued;
+      } else {
+        issue_tile(issued);
+      }
       ++issued;
     }
+  };
+  auto issue_v = [&]() {
+    if (v_pending >= 0) issue_part(v_pending, false, true);
   };
   // This wave's tile of super-tile `it` sits at stage (it % NS), slot kg.
   for (int it = 0; it + 1 < nsup; ++it) {  // full super-tiles
     advance(it);
     if constexpr (HALF)
       half_tile_step<D, false>(smem + (it % NS) * SBUF + (kg >> 1) * (TPS - 1) * TG::BUFB, kbase, vbase, qf,
-                               oacc, m_run, l_part, c, hh, BN, TPS == 2 ? (kg & 1) : kg);
+                               oacc, m_run, l_part, c, hh, BN, TPS == 2 ? (kg & 1) : kg, issue_v);
     else
       tile_step<D, false>(smem + (it % NS) * SBUF + kg * TG::BUFB, kbase, vbase, qf, oacc, m_run, l_part, c,
-                          hh, BN);
+                          hh, BN, issue_v);
     if (NPF > 0 && it == 0) {
       __asm__ volatile("" ::: "memory");  // keep these loads after the tiles issued so far
       fetch_tokens();
