@@ -34,6 +34,10 @@ CASES = {
                     dict(ONE, key_groups=1, rows_per_block=128), True),
     "kg2_rows64": (dict(R=2, B=40, Hq=8, Hkv=2, D=128, prefix_len=[513, 129], unshared_len=[5, 5]),
                    dict(ONE, key_groups=2, rows_per_block=64), True),
+    "kg4_g8_short": (dict(R=2, B=12, Hq=16, Hkv=2, D=128, prefix_len=[400, 150], unshared_len=[2, 1]),
+                     dict(ONE, key_groups=4, rows_per_block=64), True),
+    "kg4_inactive_mix": (dict(R=4, B=30, Hq=8, Hkv=2, D=128, prefix_len=[600, 70, 0, 333],
+                              unshared_len=[3, 1, 0, 2], T_max=3), dict(ONE, key_groups=4, rows_per_block=64), True),
     "kg4_rows32": (dict(R=2, B=24, Hq=8, Hkv=2, D=128, prefix_len=[300, 77], unshared_len=[2, 3]),
                    dict(ONE, key_groups=4, rows_per_block=32), True),
     "kg1_rows64_nw2": (dict(R=2, B=30, Hq=8, Hkv=2, D=128, prefix_len=[410, 64], unshared_len=[6, 2]),

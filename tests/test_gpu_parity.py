@@ -48,6 +48,7 @@ CASES = {
     "mfma_multi_tile": dict(R=2, B=40, Hq=8, Hkv=2, D=128, prefix_len=[700, 333], unshared_len=[4, 2]),
     "d64_bf16": dict(R=2, B=24, Hq=4, Hkv=1, D=64, prefix_len=[257, 130], unshared_len=[2, 3]),
     "g8_bf16": dict(R=2, B=16, Hq=16, Hkv=2, D=128, prefix_len=[520, 64], unshared_len=[5, 1]),
+    "g16_bf16": dict(R=2, B=6, Hq=32, Hkv=2, D=128, prefix_len=[450, 130], unshared_len=[3, 2]),
     "g1_bf16": dict(R=2, B=20, Hq=2, Hkv=2, D=128, prefix_len=[99, 200], unshared_len=[1, 3]),
     "g6_bf16": dict(R=1, B=9, Hq=12, Hkv=2, D=128, prefix_len=[131], unshared_len=[2]),
     "b1_decode_bf16": dict(R=5, B=1, Hq=8, Hkv=2, D=128, prefix_len=[300, 64, 1, 0, 500], unshared_len=[3, 0, 2, 4, 1], T_max=5),
@@ -82,7 +83,7 @@ def test_decode_forced_splits(splits):
     compare(o, O, lse, L, "bf16", f"decode splits={splits} plan={plan}")
 
 
-KG_CASES = ["ragged_small_bf16", "mfma_multi_tile", "d64_bf16", "g8_bf16", "g6_bf16", "no_prefix_bf16",
+KG_CASES = ["ragged_small_bf16", "mfma_multi_tile", "d64_bf16", "g8_bf16", "g16_bf16", "g6_bf16", "no_prefix_bf16",
             "no_gen_bf16", "long_gen_bf16"]
 
 
