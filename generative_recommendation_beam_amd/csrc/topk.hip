@@ -14,7 +14,10 @@
 //     part in the next round only while its last scanned candidate still
 //     reaches tau (early termination). Candidates with key >= tau are
 //     appended to LDS.
-//  3. Sort the survivors (bitonic, in LDS) and emit the n_out largest.
+//  3. Order the survivors and emit the n_out largest: for n_out <= 128,
+//     waves sort runs of 128 in registers and pairwise merges keep the best
+//     128; otherwise one wave sorts up to 1024 in registers, or the
+//     workgroup sorts in LDS.
 // If the survivors do not fit in LDS (many exact ties), a slower exact path
 // merges blocks of beams into a running best set instead.
 #include "device.h"
@@ -81,10 +84,37 @@ __device__ __forceinline__ void store_regs(const uint64_t* v, uint64_t* keys, in
   }
 }
 
+// The value lane ^ lm holds (lm a power of two below 64), by ALU lane
+// exchanges only: data-parallel row permutes for 1, 2, 4 and 8, the
+// half-swapping lane permutes for 16 and 32.
+__device__ __forceinline__ uint32_t xor_lanes32(uint32_t v, int lm) {
+  const int x = (int)v;
+  switch (lm) {
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    case 4:  // half-row mirror (lane ^ 7), then quad_perm [3,2,1,0] (lane ^ 3)
+      return (uint32_t)__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false), 0x1B, 0xF,
+                                                0xF, false);
+    case 8: return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row rotate by 8
+    case 16: {  // odd 16-lane rows of one copy swapped with even rows of the other
+      const auto w = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      return (threadIdx.x & 16) ? w[0] : w[1];
+    }
+    default: {  // upper 32 lanes of one copy swapped with the lower 32 of the other
+      const auto w = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return (threadIdx.x & 32) ? w[0] : w[1];
+    }
+  }
+}
+
+__device__ __forceinline__ uint64_t xor_lanes(uint64_t v, int lm) {
+  return ((uint64_t)xor_lanes32((uint32_t)(v >> 32), lm) << 32) | xor_lanes32((uint32_t)v, lm);
+}
+
 // Bitonic sort of 64 * S keys held by one wavefront, S per lane (element
 // e = S * lane + s), into descending order: strides below S swap inside a
-// lane, larger ones pair lanes through shuffles. No barrier and no LDS, which
-// for a few hundred keys beats the workgroup sort's barrier-bound stages.
+// lane, larger ones pair lanes through lane exchanges. No barrier and no
+// LDS. The whole wavefront must be active.
 template <int S>
 __device__ __forceinline__ void wave_sort_desc(uint64_t* v) {
   const int lane = threadIdx.x & 63;
@@ -108,13 +138,73 @@ __device__ __forceinline__ void wave_sort_desc(uint64_t* v) {
 #pragma unroll
         for (int s = 0; s < S; ++s) {
           const int e = S * lane + s;
-          const uint64_t p = __shfl_xor(v[s], lm);
+          const uint64_t p = xor_lanes(v[s], lm);
           const bool keep_max = ((e & size) == 0) == ((e & stride) == 0);
           v[s] = keep_max ? (v[s] > p ? v[s] : p) : (v[s] < p ? v[s] : p);
         }
       }
     }
   }
+}
+
+// The n_keep (<= 128) largest of n (<= 1024) keys (key i = key_of(i)) into
+// out[0, n_keep), in descending order; runs[0, 1024) is LDS scratch (out may
+// be runs itself, then n_keep = 0 and run 0 holds the result). Waves
+// 0 .. nr-1 each sort a run of 128 keys in registers, two per lane; then
+// rounds of pairwise merges keep the 128 largest of two runs: with A and B
+// descending, max(A[i], B[127 - i]) is a bitonic sequence holding exactly
+// the 128 largest of both, which one bitonic merge puts in order. Whole
+// workgroup (16 waves); ends with a barrier.
+template <typename F>
+__device__ void top128_to(F&& key_of, int n, uint64_t* runs, uint64_t* out, int n_keep) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int nr = (n + 127) >> 7;
+  if (wave < nr) {  // uniform per wave
+    uint64_t v[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int e = 128 * wave + 2 * lane + s;
+      v[s] = e < n ? key_of(e) : 0ull;
+    }
+    wave_sort_desc<2>(v);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) runs[128 * wave + 2 * lane + s] = v[s];
+  }
+  __syncthreads();
+  while (nr > 1) {
+    const int nk = (nr + 1) >> 1;  // run k = best 128 of runs 2k and 2k+1 (a missing one is all zeros)
+    uint64_t v[2];
+    if (wave < nk) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int i = 2 * lane + s;
+        const uint64_t x = runs[256 * wave + i];
+        const uint64_t y = 2 * wave + 1 < nr ? runs[256 * wave + 255 - i] : 0ull;
+        v[s] = x > y ? x : y;
+      }
+#pragma unroll
+      for (int stride = 64; stride >= 2; stride >>= 1) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const uint64_t p = xor_lanes(v[s], stride >> 1);
+          const bool keep_max = ((2 * lane + s) & stride) == 0;
+          v[s] = keep_max ? (v[s] > p ? v[s] : p) : (v[s] < p ? v[s] : p);
+        }
+      }
+      const uint64_t hi = v[0] > v[1] ? v[0] : v[1];
+      v[1] = v[0] > v[1] ? v[1] : v[0];
+      v[0] = hi;
+    }
+    __syncthreads();  // every read of this round before any write
+    if (wave < nk) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) runs[128 * wave + 2 * lane + s] = v[s];
+    }
+    __syncthreads();
+    nr = nk;
+  }
+  for (int i = threadIdx.x; i < n_keep; i += blockDim.x) out[i] = runs[i];
+  __syncthreads();
 }
 
 // The n (<= 64 * S) keys of keys_in[] (or computed by key_of(i)) sorted by
@@ -178,6 +268,19 @@ __global__ __launch_bounds__(kThreads) void beam_topk_kernel(TopkArgs a) {
   const float* bs = a.beam_score + (int64_t)r * BW;
   const float* lp = a.logprob + (int64_t)r * BW * K;
 
+  // Round 0 of the walk (below) scans the first kChunk candidates of every
+  // beam, thread t taking four of them; they do not depend on the seed, so
+  // they are requested now (indices clamped; unused ones are ignored).
+  constexpr int Q0 = kChunk / 4;
+  float pre_sb, pre_l[4];
+  {
+    const int u = min(tid, BW * Q0 - 1);
+    const int b = u / Q0, k0 = 4 * (u - b * Q0);
+    pre_sb = bs[b];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pre_l[e] = lp[(int64_t)b * K + min(k0 + e, K - 1)];
+  }
+
   // 1. Seed threshold from a sample: the best m candidates of every beam
   //    (m chosen so the sample holds about 4 * n_out keys and fits in LDS).
   //    Its n_out-th largest key bounds the pool's from below.
@@ -190,7 +293,9 @@ __global__ __launch_bounds__(kThreads) void beam_topk_kernel(TopkArgs a) {
       const int b = i / m, k = i - (i / m) * m;
       return make_key(bs[b] + lp[(int64_t)b * K + k], (uint32_t)b * (uint32_t)K + (uint32_t)k);
     };
-    if (n_s <= 512) {
+    if (N <= 128 && n_s <= 1024) {
+      top128_to(sample, n_s, keys, keys, 0);
+    } else if (n_s <= 512) {
       wave_sort_to<8>(sample, n_s, keys, N);
     } else if (n_s <= 1024) {
       wave_sort_to<16>(sample, n_s, keys, N);
@@ -222,35 +327,60 @@ __global__ __launch_bounds__(kThreads) void beam_topk_kernel(TopkArgs a) {
   for (int round = 0;; ++round) {
     const int chunk = round == 0 ? kChunk : max(kChunk, ((kThreads * 4) / n_act) & ~3);
     const int Q = chunk / 4;
-    for (int u = tid; u < n_act * Q; u += kThreads) {
-      const int ai = u / Q, q = u - ai * Q;
-      const int b = round == 0 ? ai : act[round & 1][ai];
-      const float sb = bs[b];
+    const int nu = n_act * Q;
+    const int lane = tid & 63;
+    const uint64_t below = (1ull << lane) - 1;  // lanes below this one
+    // Whole waves iterate together, so the appends go through one LDS atomic
+    // per wave (a ballot-based prefix sum places each lane's keys).
+    for (int u0 = 0; u0 < nu; u0 += kThreads) {
+      const int u = u0 + tid;
+      const bool on = u < nu;
+      const int uc = on ? u : 0;
+      const int ai = uc / Q, q = uc - ai * Q;
+      const int b = round == 0 ? ai : min(max(act[round & 1][ai], 0), BW - 1);  // (clamped: loads stay in the pool)
       const int k0 = pos + 4 * q;
+      float sb, l[4];
+      if (round == 0 && u0 == 0) {  // uniform: the prefetched candidates
+        sb = pre_sb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) l[e] = pre_l[e];
+      } else {
+        sb = bs[b];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) l[e] = lp[(int64_t)b * K + min(k0 + e, K - 1)];
+      }
       uint64_t kk[4];
       int nk = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int k = k0 + e;
-        kk[e] = 0;
-        if (k < K) {
-          kk[e] = make_key(sb + lp[(int64_t)b * K + k], (uint32_t)b * (uint32_t)K + (uint32_t)k);
-          nk += kk[e] >= tau ? 1 : 0;
-        }
+        const bool ok = on && k0 + e < K;
+        kk[e] = ok ? make_key(sb + l[e], (uint32_t)b * (uint32_t)K + (uint32_t)(k0 + e)) : 0ull;
+        nk += ok && kk[e] >= tau ? 1 : 0;
       }
-      if (nk > 0) {
-        const int at = atomicAdd(&s_count, nk);
-        int w = 0;
+      const uint64_t m0 = __ballot(nk & 1), m1 = __ballot(nk & 2), m2 = __ballot(nk & 4);
+      const int tot = __popcll(m0) + 2 * __popcll(m1) + 4 * __popcll(m2);
+      if (tot > 0) {  // uniform per wave
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&s_count, tot);
+        int at = __builtin_amdgcn_readfirstlane(base) + __popcll(m0 & below) + 2 * __popcll(m1 & below) +
+                 4 * __popcll(m2 & below);  // (every lane active here: lane 0's base)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if (k0 + e < K && kk[e] >= tau) {
-            if (at + w < kTopkCap) keys[at + w] = kk[e];
-            ++w;
+          if (on && k0 + e < K && kk[e] >= tau) {
+            if (at < kTopkCap) keys[at] = kk[e];
+            ++at;
           }
         }
       }
-      if (q == Q - 1 && k0 + 3 < K - 1 && kk[3] >= tau)
-        act[(round + 1) & 1][atomicAdd(&s_nact[(round + 1) & 1], 1)] = b;
+      // The beam goes on if its last candidate here reaches tau and more remain.
+      const bool go = on && q == Q - 1 && k0 + 3 < K - 1 && kk[3] >= tau;
+      const uint64_t mg = __ballot(go);
+      if (mg) {  // uniform per wave
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&s_nact[(round + 1) & 1], (int)__popcll(mg));
+        const int gb = __builtin_amdgcn_readfirstlane(base);  // lane 0's: read with every lane active
+        if (go) act[(round + 1) & 1][gb + __popcll(mg & below)] = b;
+      }
     }
     __syncthreads();
     n_act = s_nact[(round + 1) & 1];
@@ -269,7 +399,10 @@ __global__ __launch_bounds__(kThreads) void beam_topk_kernel(TopkArgs a) {
   if (!overflow) {
     // 3. Sort the survivors; the n_out largest lead.
     const int n = n_found;
-    if (n <= 1024) {
+    if (N <= 128 && n <= 1024) {
+      auto survivor = [&](int i) { return keys[i]; };
+      top128_to(survivor, n, reinterpret_cast<uint64_t*>(&act[0][0]), keys, N);
+    } else if (n <= 1024) {
       // One wave sorts them in registers into the other buffer (act, free
       // after the walk).
       uint64_t* sorted = reinterpret_cast<uint64_t*>(&act[0][0]);

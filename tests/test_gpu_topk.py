@@ -49,7 +49,10 @@ def test_topk_pools(dist, R, BW, K):
 
 
 @pytest.mark.parametrize("R,BW,K,n_out", [(3, 100, 37, 100), (2, 64, 64, 200), (5, 33, 1, 33),
-                                          (1, 7, 5, 35), (2, 300, 9, 150), (1, 1, 64, 16)])
+                                          (1, 7, 5, 35), (2, 300, 9, 150), (1, 1, 64, 16),
+                                          # n_out <= 128: seed samples and survivors in 1 to 8 runs of 128
+                                          (2, 300, 40, 100), (1, 1024, 4, 128), (3, 64, 128, 128),
+                                          (2, 50, 50, 1), (2, 200, 16, 127)])
 def test_topk_ragged(R, BW, K, n_out):
     check(make_topk("ragged", R=R, BW=BW, K=K, n_out=n_out, seed_key=(401, BW, K, n_out), vocab=256))
 
