@@ -312,6 +312,16 @@ hipError_t run_prefix(const xattn_dims* d, const Plan& p, int mode, const void* 
     a.table_out = fa ? fa->table_out : nullptr;
     a.ulen_rw = fa ? fa->ulen : nullptr;
     a.arrivals = d->num_kv_heads;  // per request, after each (request, kv head) has counted its row tiles
+    {
+      const int64_t row_bytes = (int64_t)d->num_kv_heads * d->head_dim * 2;
+      const int64_t new_rows = (int64_t)d->num_requests * d->beam_width;
+      const bool small_pool = (int64_t)d->num_slots * row_bytes < (int64_t(1) << 32) &&
+                              (!fa || new_rows * row_bytes < (int64_t(1) << 32));
+      a.token_block = kp != nullptr && small_pool && d->num_q_heads == 4 * d->num_kv_heads &&
+                      d->max_unshared_len <= 3 && d->head_dim == 128;
+      a.pool_bytes = small_pool ? (uint32_t)((int64_t)d->num_slots * row_bytes) : 0u;
+      a.new_bytes = (small_pool && fa) ? (uint32_t)(new_rows * row_bytes) : 0u;
+    }
     return launch_shared_mfma(a, st);
   }
   ValuArgs a;

@@ -68,6 +68,12 @@ struct SharedMfmaArgs {
   uint16_t* v_pool_out;
   int32_t* table_out;       // [N_b][T_max], not table_in
   int32_t* ulen_rw;         // = unshared_len, counted and written
+  // four key groups may take the generated tokens as one matrix-core block:
+  // four query heads per kv head, at most three generated tokens, pool and
+  // k_new byte offsets within 32 bits
+  int token_block;
+  uint32_t pool_bytes;      // with token_block: bytes of k_pool (= of v_pool)
+  uint32_t new_bytes;       // with token_block and the fused append: bytes of k_new
   int arrivals;             // kv heads per request: second-level arrivals
   // first-level arrivals: `counters` [R*H_kv], the row tiles of a (request,
   // kv head), wrapping back to zero

@@ -73,6 +73,31 @@ __device__ __forceinline__ int swz_k(int key) { return D == 128 ? (key & 15) : (
 template <int D>
 __device__ __forceinline__ int swz_v(int key) { return D == 128 ? ((key & 3) << 2) : ((key & 1) << 2); }
 
+// Per-lane LDS byte bases of the MFMA operands (see the kernel).
+template <int D>
+__device__ __forceinline__ int k_operand_base(int lane) {
+  using TG = TileGeom<D>;
+  const int ql = lane & 31, hh = lane >> 5;
+  const int f = swz_k<D>(ql);
+  return ql * TG::ROWB + 16 * (hh ^ (f & 1)) + 32 * (f >> 1);
+}
+template <int D>
+__device__ __forceinline__ int v_operand_base(int lane) {
+  using TG = TileGeom<D>;
+  const int hh = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
+  const int key0 = 4 * hh + (i16 >> 2);
+  const int x = 2 * (g16 & 1) + ((i16 & 3) >> 1);
+  return TG::TILEB + key0 * TG::ROWB + 16 * (x ^ swz_v<D>(key0)) + (i16 & 1) * 8;
+}
+
+// The lane index, computed afresh where keeping the kernel's copy (and what
+// derives from it) alive would cost registers.
+__device__ __forceinline__ int fresh_lane() {
+  int l;
+  __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // A workgroup loads KG consecutive 64-key tiles per step (a super-tile); its
 // NW waves share the KG*NINST direct-load instructions per tensor. Wave w
 // issues instructions i = w + NW*j; instruction i fills 1 KiB of tile
@@ -124,7 +149,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const float* bas
 // 16 scores this lane holds for its query column), followed by that half's
 // P.V MFMAs. Processing the halves separately lets the vector-ALU softmax of
 // one half overlap the matrix-core work of the other.
-template <int D, bool MASK>
+template <int D, bool MASK, bool NO_HI1 = false>
 __device__ __forceinline__ void half_softmax_pv(const char* buf, int vbase, f32x16_t& sb, int kb,
                                                 f32x16_t* oacc, float& m_run, float& l_part, float c,
                                                 int hh, int nvalid) {
@@ -167,7 +192,10 @@ __device__ __forceinline__ void half_softmax_pv(const char* buf, int vbase, f32x
     for (int ch = 0; ch < 2; ++ch) {
       const int vo = (vbase ^ (64 * db)) + (16 * (2 * kb + ch)) * TG::ROWB;
       const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(buf + vo));
-      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(buf + vo + 8 * TG::ROWB));
+      // NO_HI1: keys 24..31 of the half are not there (their V operand is zero)
+      const i16x4_t hi = (NO_HI1 && ch == 1)
+                             ? i16x4_t{0, 0, 0, 0}
+                             : __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(buf + vo + 8 * TG::ROWB));
       const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ch], oacc[db], 0, 0, 0);
     }
@@ -237,6 +265,37 @@ __device__ __forceinline__ void half_tile_step(const char* buf, int kbase, int v
   __builtin_amdgcn_sched_group_barrier(0x008, NDC, 0);
   after_s();
   half_softmax_pv<D, MASK>(buf, vbase, sacc, kb, oacc, m_run, l_part, c, hh, nvalid);
+}
+
+// The generated tokens of one wave's beams as one 32-key block on the matrix
+// cores. With four query heads per kv head a wave's 32 rows are 8 beams; LDS
+// row 8t + b of the block (t < 3) holds token t of beam b, K rows then V
+// rows, each in the tile layout (K rows 24..31 read whatever follows and are
+// masked; V rows 24..31 are not read). A row's score against key 8t + b is
+// kept only for its own beam b and a token t < L.
+template <int D>
+__device__ __forceinline__ void token_block_step(const char* blk, const bf16x8_t* qf, f32x16_t* oacc,
+                                                 float& m_run, float& l_part, float c, int own_beam, int L) {
+  using TG = TileGeom<D>;
+  const int lane = fresh_lane();
+  const int hh = lane >> 5;
+  const int kbase = k_operand_base<D>(lane), vbase = v_operand_base<D>(lane);
+  constexpr int NDC = D / 16;
+  f32x16_t sacc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+  bf16x8_t ka[NDC];
+#pragma unroll
+  for (int dc = 0; dc < NDC; ++dc) ka[dc] = *reinterpret_cast<const bf16x8_t*>(blk + (kbase ^ (32 * dc)));
+  __builtin_amdgcn_sched_group_barrier(0x100, NDC, 0);
+#pragma unroll
+  for (int dc = 0; dc < NDC; ++dc) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc], qf[dc], sacc, 0, 0, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, NDC, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {  // key 8 * (i / 4) + 4 * hh + i % 4: token i / 4 of beam 4 * hh + i % 4
+    if (4 * hh + (i & 3) != own_beam || (i >> 2) >= L) sacc[i] = neg_inf();
+  }
+  half_softmax_pv<D, false, true>(blk + 24 * TG::ROWB - TG::TILEB, vbase, sacc, 0, oacc, m_run, l_part, c, hh, BN);
 }
 
 // Wait until at most n vector-memory operations are in flight. The counter
@@ -372,7 +431,7 @@ __device__ __forceinline__ void store_rows(float* dst, const f32x16_t* oacc) {
 // kg: half the work per step, three steps of loads in flight. At the end the groups' softmax states are combined through
 // LDS with the log-sum-exp rule; group kg then finalizes and stores column
 // blocks [kg*NDB/KG, (kg+1)*NDB/KG) of the head dim.
-template <int D, int NW, int NS, int KG>
+template <int D, int NW, int NS, int KG, bool TB = false>
 __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(SharedMfmaArgs a,
                                                                                int64_t n_logical) {
   // The host pass only needs this kernel's signature for its launch stub.
@@ -394,7 +453,16 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   static_assert(NDB % KG == 0, "every key group finalizes whole column blocks");
   static_assert(KG == 1 || RG * NDB * (KG - 1) * 4096 + 2 * KG * RG * 32 * 4 <= NS * SBUF,
                 "the key-group exchange must fit in the stage buffers");
-  __shared__ __attribute__((aligned(1024))) char smem[NS * SBUF];
+  // TB (four key groups, four query heads per kv head, at most three
+  // generated tokens): per row group, the token block (24 K rows, 24 V rows)
+  // is moved into LDS during the prompt loop by groups 0..2 (token kg each)
+  // and group 3 runs it on the matrix cores after the loop. It sits behind
+  // the stage buffers in the same array.
+  constexpr bool LTOK = TB;
+  static_assert(!TB || (NW == 8 && KG == 4 && D == 128 && NS == 2), "token block: the four-group kernel");
+  constexpr int TOKRG = 2 * 24 * TG::ROWB;
+  __shared__ __attribute__((aligned(1024))) char smem[NS * SBUF + (TB ? RG * TOKRG : 0)];
+  char* const s_tok = smem + NS * SBUF;
   __shared__ int s_last;
   __shared__ int s_par[RG * 32 + 1];    // fused append: parents of the owned beams
 
@@ -474,6 +542,20 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   const int actv = actp[zv];
   const int parv = parp[zv];
   const int64_t sbv = sbp[zv];
+  // Token block (LTOK): for i = 0, 1 lane l moves 16-byte chunk l % 16 of
+  // block row 8 kg + 4 i + l / 16, i.e. of beam bw0 + 4 i + l / 16 (clamped
+  // to the request); with the fused append the beam's parent is requested
+  // now.
+  const bool ltok_shape = LTOK && do_ns && kg < 3;  // uniform per wave
+  const int bw0 = (tile * (RG * 32) + rg * 32) / G;  // this wave's first beam (G = 4)
+  auto tbeam = [&](int i) { return min(bw0 + 4 * i + (lane >> 4), s.B - 1); };
+  int tref[2] = {0, 0};
+  if constexpr (LTOK) {
+    if (ltok_shape && app) {  // uniform
+#pragma unroll
+      for (int i = 0; i < 2; ++i) tref[i] = a.parent[(int64_t)r * s.B + tbeam(i)];
+    }
+  }
   bf16x8_t qf[NDC];
   {
     const uint16_t* qp = a.q + qrow * D + 8 * hh;
@@ -591,6 +673,61 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
 #pragma unroll
     for (int u = 0; u < NSL; ++u) pslot[u] = ns.slot(u);
   }
+  // Token block: every group holds at most one token (L <= 3); group kg < 3
+  // moves token min(kg, L - 1) (a repeat is masked out), from the pool
+  // through the slot table - with the fused append through the parent's
+  // row, or from k_new/v_new for the new token.
+  const bool ltok = LTOK && do_ns && ns.L >= 1;  // uniform
+  const int tk = min(kg, ns.L - 1);
+  const bool tk_new = tk == ns.tnew;
+  if constexpr (LTOK) {
+    if (ltok && kg < 3 && !tk_new) {  // uniform per wave
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        tref[i] = a.slot_table[((int64_t)r * s.B + ((app && grow) ? tref[i] : tbeam(i))) * s.T_max + tk];
+    }
+  }
+  // The token rows go through registers (16-byte chunks, natural order) and
+  // are written to LDS in the tile layout after the loop: a direct-to-LDS
+  // load inside the loop would make the compiler wait for every outstanding
+  // load before each step's LDS reads.
+  u32x4_t tkv[2][2];  // [K, V][i]
+  auto issue_tok = [&]() {
+    if constexpr (LTOK) {
+      if (!ltok || kg >= 3) return;  // uniform
+      // bounded to the pool (or the new rows): an out-of-range slot reads zeros
+      const int nrec = (int)(tk_new ? a.new_bytes : a.pool_bytes);
+      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(tk_new ? a.k_new : a.k_pool), (short)0, nrec, 0x00020000);
+      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(tk_new ? a.v_new : a.v_pool), (short)0, nrec, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int64_t row = tk_new ? ((int64_t)r * s.B + tbeam(i)) * s.Hkv + h : (int64_t)tref[i] * s.Hkv + h;
+        const uint32_t off = (uint32_t)(row * TG::ROWB) + (uint32_t)((lane & 15) * 16);
+        tkv[0][i] = __builtin_amdgcn_raw_buffer_load_b128(kr, (int)off, 0, 0);
+        tkv[1][i] = __builtin_amdgcn_raw_buffer_load_b128(vr, (int)off, 0, 0);
+      }
+    }
+  };
+  // After the loop: lane l holds chunk l % 16 of rows 8 kg + 4 i + l / 16.
+  auto store_tok = [&]() {
+    if constexpr (LTOK) {
+      if (!ltok || kg >= 3) return;  // uniform
+      char* tK = s_tok + rg * TOKRG;
+      char* tV = tK + 24 * TG::ROWB;
+      const int c = lane & 15;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int j = 8 * kg + 4 * i + (lane >> 4);
+        *reinterpret_cast<u32x4_t*>(tK + j * TG::ROWB + 16 * (c ^ swz_k<D>(j))) = tkv[0][i];
+        *reinterpret_cast<u32x4_t*>(tV + j * TG::ROWB + 16 * (c ^ swz_v<D>(j))) = tkv[1][i];
+      }
+    }
+  };
+  // Requested at the start of the step before the last (measured faster than
+  // with the first step's or the last step's loads).
+  const int tok_at = max(nsup - 2, 0);
 
 
   f32x16_t oacc[NDB];
@@ -603,24 +740,13 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
 
   // Per-lane LDS byte bases. K operand (kb, dc): key 32*kb + ql, chunk
   // 2*dc + hh, at base_k ^ (32*dc) + kb*32*ROWB.
-  int kbase;
-  {
-    const int f = swz_k<D>(ql);
-    kbase = ql * TG::ROWB + 16 * (hh ^ (f & 1)) + 32 * (f >> 1);
-  }
+  const int kbase = k_operand_base<D>(lane);
   // V^T operand via ds_read_b64_tr_b16 (db, cc, half j4): within each group of
   // 16 lanes, source lane i points at key 16*cc + 8*j4 + 4*hh + i/4,
   // head-dim elements 32*db + 16*(g&1) + 4*(i%4) .. +4, so result lane i
   // receives those four keys at head-dim element 32*db + 16*(g&1) + i.
   // Address: (base_v ^ (64*db)) + (16*cc + 8*j4)*ROWB.
-  const int g16 = lane >> 4, i16 = lane & 15;
-  int vbase;
-  {
-    const int e = i16 >> 2;
-    const int key0 = 4 * hh + e;
-    const int x = 2 * (g16 & 1) + ((i16 & 3) >> 1);
-    vbase = TG::TILEB + key0 * TG::ROWB + 16 * (x ^ swz_v<D>(key0)) + (i16 & 1) * 8;
-  }
+  const int vbase = v_operand_base<D>(lane);
 
   // Wait for super-tile `it`, then refill the buffer super-tile it-1 used.
   // The token rows (when fetched inside the loop) follow the loads of
@@ -640,6 +766,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
     else
       wait_tiles<LPT>(min(issued - 1 - it, NS - 2));
     __syncthreads();  // super-tile `it` landed for every wave; it-1's buffer is free
+    if (it == tok_at) issue_tok();  // before the refill: nothing is in flight here
     v_pending = -1;
     if (issued < nsup) {
       if constexpr (NS == 2 && HALF) {
@@ -687,7 +814,10 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
     }
   }
 
+  if (nsup == 0) issue_tok();
   wait_vmem();  // every tile load has landed before the stage buffers are reused
+  store_tok();
+  if (ltok) __syncthreads();  // the token block is complete in LDS
 
   // Fused append writes: the first K/V chunk (loaded in the prologue) is
   // stored now; the first table cells are requested before the tokens' rows
@@ -741,7 +871,11 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
 #pragma unroll
   for (int u = 0; u < NPF; ++u)
     if (ns.has(u)) token_update<D>(pk[u], pv[u], qf, oacc, m_run, l_part, c, hh);
-  if (ns.has(NPF)) {
+  if constexpr (TB) {
+    if (ltok && kg == 3)  // uniform
+      token_block_step<D>(s_tok + rg * TOKRG, qf, oacc, m_run, l_part, c,
+                          (tile * (RG * 32) + rg * 32 + (fresh_lane() & 31)) / G - bw0, ns.L);
+  } else if (ns.has(NPF)) {
     int sl = NPF == 0 ? pslot[0] : ns.slot(NPF);
     for (int u = NPF; u < NonShared<D, KG>::NT && ns.has(u); ++u) {
       uint4 kk[NDC];
@@ -947,6 +1081,13 @@ hipError_t launch_dwk(const SharedMfmaArgs& a, int64_t grid, int64_t n_logical, 
   if constexpr (KG != 4) {
     if (a.stages == 4) {
       hipLaunchKernelGGL((shared_mfma_kernel<D, NW, 4, KG>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a,
+                         n_logical);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (D == 128 && NW == 8 && KG == 4) {
+    if (a.token_block) {
+      hipLaunchKernelGGL((shared_mfma_kernel<D, NW, 2, KG, true>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a,
                          n_logical);
       return hipGetLastError();
     }

@@ -48,6 +48,10 @@ CASES = {
     "mfma_multi_tile": dict(R=2, B=40, Hq=8, Hkv=2, D=128, prefix_len=[700, 333], unshared_len=[4, 2]),
     "d64_bf16": dict(R=2, B=24, Hq=4, Hkv=1, D=64, prefix_len=[257, 130], unshared_len=[2, 3]),
     "g8_bf16": dict(R=2, B=16, Hq=16, Hkv=2, D=128, prefix_len=[520, 64], unshared_len=[5, 1]),
+    # four query heads per kv head, at most three generated tokens: with four
+    # key groups the tokens go through one matrix-core block (lengths 0..3,
+    # prompts of 0, 1 and several 128-key steps)
+    "tb_mix_bf16": dict(R=4, B=30, Hq=8, Hkv=2, D=128, prefix_len=[600, 70, 0, 129], unshared_len=[3, 1, 2, 0]),
     "g16_bf16": dict(R=2, B=6, Hq=32, Hkv=2, D=128, prefix_len=[450, 130], unshared_len=[3, 2]),
     "g1_bf16": dict(R=2, B=20, Hq=2, Hkv=2, D=128, prefix_len=[99, 200], unshared_len=[1, 3]),
     "g6_bf16": dict(R=1, B=9, Hq=12, Hkv=2, D=128, prefix_len=[131], unshared_len=[2]),
@@ -84,6 +88,7 @@ def test_decode_forced_splits(splits):
 
 
 KG_CASES = ["ragged_small_bf16", "mfma_multi_tile", "d64_bf16", "g8_bf16", "g16_bf16", "g6_bf16", "no_prefix_bf16",
+            "tb_mix_bf16",
             "no_gen_bf16", "long_gen_bf16"]
 
 
