@@ -14,10 +14,10 @@
 //     part in the next round only while its last scanned candidate still
 //     reaches tau (early termination). Candidates with key >= tau are
 //     appended to LDS.
-//  3. Order the survivors and emit the n_out largest: for n_out <= 128,
-//     waves sort runs of 128 in registers and pairwise merges keep the best
-//     128; otherwise one wave sorts up to 1024 in registers, or the
-//     workgroup sorts in LDS.
+//  3. Order the survivors and emit the n_out largest: for n_out <= 512,
+//     waves sort runs of 128, 256 or 512 keys in registers and pairwise
+//     merges keep the best run; otherwise one wave sorts up to 1024 in
+//     registers, or the workgroup sorts in LDS.
 // If the survivors do not fit in LDS (many exact ties), a slower exact path
 // merges blocks of beams into a running best set instead.
 #include "device.h"
@@ -113,10 +113,9 @@ __device__ __forceinline__ uint32_t xor_lanes32(uint32_t v, int lm) {
 // sorts, where it was 1.5-2.4x faster.
 template <bool ALU>
 __device__ __forceinline__ uint64_t xor_lanes(uint64_t v, int lm) {
-  if constexpr (ALU)
+  if (ALU && __builtin_constant_p(lm))  // (a run-time lm would branch per exchange)
     return ((uint64_t)xor_lanes32((uint32_t)(v >> 32), lm) << 32) | xor_lanes32((uint32_t)v, lm);
-  else
-    return __shfl_xor(v, lm);
+  return __shfl_xor(v, lm);
 }
 
 // Bitonic sort of 64 * S keys held by one wavefront, S per lane (element
@@ -155,64 +154,108 @@ __device__ __forceinline__ void wave_sort_desc(uint64_t* v) {
   }
 }
 
-// The n_keep (<= 128) largest of n (<= 1024) keys (key i = key_of(i)) into
-// out[0, n_keep), in descending order; runs[0, 1024) is LDS scratch (out may
-// be runs itself, then n_keep = 0 and run 0 holds the result). Waves
-// 0 .. nr-1 each sort a run of 128 keys in registers, two per lane; then
-// rounds of pairwise merges keep the 128 largest of two runs: with A and B
-// descending, max(A[i], B[127 - i]) is a bitonic sequence holding exactly
-// the 128 largest of both, which one bitonic merge puts in order. Whole
-// workgroup (16 waves); ends with a barrier.
-template <typename F>
-__device__ void top128_to(F&& key_of, int n, uint64_t* runs, uint64_t* out, int n_keep) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int nr = (n + 127) >> 7;
-  if (wave < nr) {  // uniform per wave
-    uint64_t v[2];
+// The same network, generated at compile time (every lane distance a
+// constant, so the ALU exchanges apply): stage STRIDE of the merge of
+// descending runs of SIZE, or of one descending merge when SIZE = 0.
+template <int S, bool ALU, int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_stage(uint64_t* v, int lane) {
+  if constexpr (STRIDE < S) {  // inside a lane
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int e = 128 * wave + 2 * lane + s;
+    for (int s = 0; s < S; ++s) {
+      if (s & STRIDE) continue;
+      const int e = S * lane + s;
+      const bool desc = SIZE == 0 || (e & SIZE) == 0;
+      const uint64_t a = v[s], b = v[s + STRIDE];
+      const bool swap = desc ? a < b : a > b;
+      v[s] = swap ? b : a;
+      v[s + STRIDE] = swap ? a : b;
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int e = S * lane + s;
+      const uint64_t p = xor_lanes<ALU>(v[s], STRIDE / S);
+      const bool keep_max = (SIZE == 0 || (e & SIZE) == 0) == ((e & STRIDE) == 0);
+      v[s] = keep_max ? (v[s] > p ? v[s] : p) : (v[s] < p ? v[s] : p);
+    }
+  }
+}
+template <int S, bool ALU, int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_stages(uint64_t* v, int lane) {  // STRIDE, STRIDE / 2, ..., 1
+  bitonic_stage<S, ALU, SIZE, STRIDE>(v, lane);
+  if constexpr (STRIDE > 1) bitonic_stages<S, ALU, SIZE, STRIDE / 2>(v, lane);
+}
+template <int S, bool ALU, int SIZE = 2>
+__device__ __forceinline__ void bitonic_sort_desc(uint64_t* v, int lane) {
+  bitonic_stages<S, ALU, SIZE, SIZE / 2>(v, lane);
+  if constexpr (SIZE < 64 * S) bitonic_sort_desc<S, ALU, SIZE * 2>(v, lane);
+}
+
+// The n_keep (<= RL = 64 S) largest of n (<= 16 RL) keys (key i =
+// key_of(i)) into out[0, n_keep), in descending order; runs[0, 16 RL) is LDS
+// scratch (out may be runs itself, then n_keep = 0 and run 0 holds the
+// result). Waves 0 .. nr-1 each sort a run of RL keys in registers, S per
+// lane; then rounds of pairwise merges keep the RL largest of two runs: with
+// A and B descending, max(A[i], B[RL-1-i]) is a bitonic sequence holding
+// exactly the RL largest of both, which one bitonic merge puts in order.
+// Whole workgroup (16 waves); ends with a barrier.
+template <int S, typename F>
+__device__ void topn_to(F&& key_of, int n, uint64_t* runs, uint64_t* out, int n_keep) {
+  constexpr int RL = 64 * S;
+  constexpr bool ALU = S <= 2;  // lane exchanges: ALU for two keys per lane, LDS permutes above (measured)
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int nr = (n + RL - 1) / RL;
+  if (wave < nr) {  // uniform per wave
+    uint64_t v[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int e = RL * wave + S * lane + s;
       v[s] = e < n ? key_of(e) : 0ull;
     }
-    wave_sort_desc<2, true>(v);
+    bitonic_sort_desc<S, ALU>(v, lane);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) runs[128 * wave + 2 * lane + s] = v[s];
+    for (int s = 0; s < S; ++s) runs[RL * wave + S * lane + s] = v[s];
   }
   __syncthreads();
   while (nr > 1) {
-    const int nk = (nr + 1) >> 1;  // run k = best 128 of runs 2k and 2k+1 (a missing one is all zeros)
-    uint64_t v[2];
+    const int nk = (nr + 1) >> 1;  // run k = best RL of runs 2k and 2k+1 (a missing one is all zeros)
+    uint64_t v[S];
     if (wave < nk) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int i = 2 * lane + s;
-        const uint64_t x = runs[256 * wave + i];
-        const uint64_t y = 2 * wave + 1 < nr ? runs[256 * wave + 255 - i] : 0ull;
+      for (int s = 0; s < S; ++s) {
+        const int i = S * lane + s;
+        const uint64_t x = runs[2 * RL * wave + i];
+        const uint64_t y = 2 * wave + 1 < nr ? runs[2 * RL * wave + 2 * RL - 1 - i] : 0ull;
         v[s] = x > y ? x : y;
       }
-#pragma unroll
-      for (int stride = 64; stride >= 2; stride >>= 1) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const uint64_t p = xor_lanes<true>(v[s], stride >> 1);
-          const bool keep_max = ((2 * lane + s) & stride) == 0;
-          v[s] = keep_max ? (v[s] > p ? v[s] : p) : (v[s] < p ? v[s] : p);
-        }
-      }
-      const uint64_t hi = v[0] > v[1] ? v[0] : v[1];
-      v[1] = v[0] > v[1] ? v[1] : v[0];
-      v[0] = hi;
+      bitonic_stages<S, ALU, 0, RL / 2>(v, lane);
     }
     __syncthreads();  // every read of this round before any write
     if (wave < nk) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) runs[128 * wave + 2 * lane + s] = v[s];
+      for (int s = 0; s < S; ++s) runs[RL * wave + S * lane + s] = v[s];
     }
     __syncthreads();
     nr = nk;
   }
   for (int i = threadIdx.x; i < n_keep; i += blockDim.x) out[i] = runs[i];
   __syncthreads();
+}
+
+// topn_to with the smallest run that holds n_keep (<= 512) keys; false (and
+// nothing done) when the n keys need more than 16 runs or n_keep > 512.
+template <typename F>
+__device__ bool topn_any(F&& key_of, int n, uint64_t* runs, uint64_t* out, int n_keep, int N) {
+  if (N <= 128 && n <= 16 * 128) {
+    topn_to<2>(key_of, n, runs, out, n_keep);
+  } else if (N <= 256 && n <= 16 * 256) {
+    topn_to<4>(key_of, n, runs, out, n_keep);
+  } else if (N <= 512 && n <= 16 * 512) {
+    topn_to<8>(key_of, n, runs, out, n_keep);
+  } else {
+    return false;
+  }
+  return true;
 }
 
 // The n (<= 64 * S) keys of keys_in[] (or computed by key_of(i)) sorted by
@@ -301,8 +344,8 @@ __global__ __launch_bounds__(kThreads) void beam_topk_kernel(TopkArgs a) {
       const int b = i / m, k = i - (i / m) * m;
       return make_key(bs[b] + lp[(int64_t)b * K + k], (uint32_t)b * (uint32_t)K + (uint32_t)k);
     };
-    if (N <= 128 && n_s <= 1024) {
-      top128_to(sample, n_s, keys, keys, 0);
+    if (topn_any(sample, n_s, keys, keys, 0, N)) {
+      // run 0 (keys[0, N)) holds the sample's best, in order
     } else if (n_s <= 512) {
       wave_sort_to<8>(sample, n_s, keys, N);
     } else if (n_s <= 1024) {
@@ -407,14 +450,13 @@ __global__ __launch_bounds__(kThreads) void beam_topk_kernel(TopkArgs a) {
   if (!overflow) {
     // 3. Sort the survivors; the n_out largest lead.
     const int n = n_found;
-    if (N <= 128 && n <= 1024) {
-      auto survivor = [&](int i) { return keys[i]; };
-      top128_to(survivor, n, reinterpret_cast<uint64_t*>(&act[0][0]), keys, N);
+    auto survivor = [&](int i) { return keys[i]; };
+    if (topn_any(survivor, n, reinterpret_cast<uint64_t*>(&act[0][0]), keys, N, N)) {
+      // keys[0, N): the survivors' best, in order (runs in act, free after the walk)
     } else if (n <= 1024) {
       // One wave sorts them in registers into the other buffer (act, free
       // after the walk).
       uint64_t* sorted = reinterpret_cast<uint64_t*>(&act[0][0]);
-      auto survivor = [&](int i) { return keys[i]; };
       if (n <= 512)
         wave_sort_to<8>(survivor, n, sorted, N);
       else
