@@ -122,7 +122,7 @@ __device__ __forceinline__ uint64_t xor_lanes(uint64_t v, int lm) {
 // e = S * lane + s), into descending order: strides below S swap inside a
 // lane, larger ones pair lanes through lane exchanges. No barrier and no
 // LDS. The whole wavefront must be active.
-template <int S, bool ALU = false>
+template <int S>
 __device__ __forceinline__ void wave_sort_desc(uint64_t* v) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -145,7 +145,7 @@ __device__ __forceinline__ void wave_sort_desc(uint64_t* v) {
 #pragma unroll
         for (int s = 0; s < S; ++s) {
           const int e = S * lane + s;
-          const uint64_t p = xor_lanes<ALU>(v[s], lm);
+          const uint64_t p = __shfl_xor(v[s], lm);
           const bool keep_max = ((e & size) == 0) == ((e & stride) == 0);
           v[s] = keep_max ? (v[s] > p ? v[s] : p) : (v[s] < p ? v[s] : p);
         }
