@@ -19,7 +19,11 @@ constexpr int kTargetWaves = 2048;     // vector path: resident waves to cover 2
 // on MI355X, a split's partial write and in-kernel merge cost more than the
 // extra parallelism returns once half the CUs hold a workgroup.
 constexpr int kTargetMfmaBlocks = 128;
-constexpr int kMinSplitKeys = 256;     // never split the prompt finer than this
+constexpr int kMinSplitKeys = 256;     // MFMA path: never split the prompt finer than this
+// Vector path: a wave walks its keys a few rows per memory round trip, so a
+// short prompt over few waves is latency-bound; splits down to this many keys
+// (merged by one more launch) pay off there.
+constexpr int kMinSplitKeysValu = 64;
 constexpr int kFuseMaxUnshared = 16;   // T_max up to this: Non-Shared part in the epilogue
 constexpr int kUnsharedChunk = 64;     // generated tokens per Non-Shared split
 constexpr int kMfmaMinRows = 16;       // fewer query rows per (r,h): vector path
@@ -129,7 +133,7 @@ Plan make_plan(const xattn_dims* d, int which) {
       s = d->prefix_splits;
     } else {
       s = base_units > 0 ? (int)cdiv(target_units, base_units) : 1;
-      s = (int)std::min<int64_t>(s, std::max<int64_t>(1, cdiv(maxP, kMinSplitKeys)));
+      s = (int)std::min<int64_t>(s, std::max<int64_t>(1, cdiv(maxP, p.mfma ? kMinSplitKeys : kMinSplitKeysValu)));
       s = std::max(s, 1);
     }
     p.p_chunk = std::max(64, (int)cdiv(cdiv(std::max(maxP, 1), s), 64) * 64);
