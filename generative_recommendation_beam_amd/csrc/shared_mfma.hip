@@ -15,7 +15,7 @@
 //    sum are lane-local except one exchange between the two lane halves;
 //  - P^T (bf16) feeds the next MFMA straight from those registers; the V^T
 //    operand is read from row-major V in LDS with ds_read_b64_tr_b16.
-// K/V tiles (64 keys) move HBM -> LDS with global_load_lds_dwordx4 (no
+// K/V tiles (64 keys) move HBM -> LDS with buffer_load_dwordx4 ... lds (no
 // register staging), double-buffered so tile i+1 is in flight while tile i is
 // computed.
 //
@@ -24,9 +24,11 @@
 // probability <= 256 and skips most output rescales; the result is exact
 // either way because the final division uses the same offset.
 //
-// Non-Shared part (prompt split 0 only, when fused): the beam's own generated
-// tokens, gathered through its slot-table row, initialise the softmax state
-// while the first K/V tile is in flight.
+// Non-Shared part (prompt split 0, or a member of its own, when fused): the
+// beam's own generated tokens, gathered through its slot-table row, join the
+// same softmax state after the prompt tiles - per wave on the vector ALU, or,
+// with four key groups, four query heads per kv head and at most three
+// tokens, as one masked 32-key block on the matrix cores.
 //
 // Prompt splits: with p_splits > 1 and mode FIXUP, every split writes its
 // partial (normalized O, lse) to the workspace, and the last workgroup of a
