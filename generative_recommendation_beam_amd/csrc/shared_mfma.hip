@@ -819,7 +819,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   if (nsup == 0) issue_tok();
   wait_vmem();  // every tile load has landed before the stage buffers are reused
   store_tok();
-  if (ltok) __syncthreads();  // the token block is complete in LDS
+  if (ltok) __syncthreads();  // the token block is complete in LDS; the stage buffers are free
 
   // Fused append writes: the first K/V chunk (loaded in the prologue) is
   // stored now; the first table cells are requested before the tokens' rows
@@ -913,7 +913,10 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
       const int owner = db / NDBW;
       return (rg * NDB + db) * (KG - 1) + (src < owner ? src : src - 1);
     };
-    __syncthreads();  // every wave is done reading the stage buffers
+    // Every wave is done reading the stage buffers. (With the token block the
+    // barrier after the loop already said so: the block reads only its own
+    // LDS, so the other groups write their exchange data while it runs.)
+    if (!(TB && ltok)) __syncthreads();
     if (hh == 0) {
       xm[(kg * RG + rg) * 32 + ql] = m_run;
       xl[(kg * RG + rg) * 32 + ql] = l_tot;
