@@ -125,6 +125,11 @@ def test_plan_introspection(L):
     assert p2["unshared_splits"] > 0 and p2["partials"] == p2["prefix_splits"] + p2["unshared_splits"]
     p3 = xattn.get_plan(dims(dtype=xattn.XATTN_F32), 2)
     assert p3["mfma"] == 0
+    # the vector path splits a short prompt over few waves down to 64 keys
+    # (one wave walks a few keys per memory round trip)
+    p4 = xattn.get_plan(dims(R=1, B=4, Hq=4, Hkv=1, D=64, max_prefix_len=256, max_unshared_len=2,
+                             dtype=xattn.XATTN_F32), 2)
+    assert p4["mfma"] == 0 and p4["prefix_splits"] == 4 and p4["prefix_chunk"] == 64
     # enough workgroups already: one key group
     p5 = xattn.get_plan(dims(R=16, B=256, Hq=64, Hkv=8, max_prefix_len=16384, max_unshared_len=8), 2)
     assert p5["key_groups"] == 1 and p5["rows_per_block"] == 128
