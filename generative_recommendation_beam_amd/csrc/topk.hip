@@ -107,10 +107,9 @@ __device__ __forceinline__ uint32_t xor_lanes32(uint32_t v, int lm) {
   }
 }
 
-// ALU: the ALU exchanges above (lm a compile-time constant after unrolling);
-// else one LDS permute. Measured: the ALU form for the 128-key runs and
-// merges (2 keys per lane), the LDS form for the 8- and 16-key-per-lane
-// sorts, where it was 1.5-2.4x faster.
+// ALU: the ALU exchanges above where lm is a compile-time constant (the
+// generated networks below); else one LDS permute (a run-time lm would
+// branch per exchange).
 template <bool ALU>
 __device__ __forceinline__ uint64_t xor_lanes(uint64_t v, int lm) {
   if (ALU && __builtin_constant_p(lm))  // (a run-time lm would branch per exchange)
@@ -202,7 +201,7 @@ __device__ __forceinline__ void bitonic_sort_desc(uint64_t* v, int lane) {
 template <int S, typename F>
 __device__ void topn_to(F&& key_of, int n, uint64_t* runs, uint64_t* out, int n_keep) {
   constexpr int RL = 64 * S;
-  constexpr bool ALU = S <= 2;  // lane exchanges: ALU for two keys per lane, LDS permutes above (measured)
+  constexpr bool ALU = true;  // compile-time networks: ALU lane exchanges (measured faster for 2, 4 and 8 keys per lane)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int nr = (n + RL - 1) / RL;
   if (wave < nr) {  // uniform per wave
