@@ -42,13 +42,16 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3       # fp32 vector
 
-DEFAULT_LAYERS = {"1": 16, "2": 16, "3": 6, "4A": 3, "4B": 2, "5": 2}
+DEFAULT_LAYERS = {"1": 16, "2": 16, "3": 6, "4A": 3, "4B": 2, "4B2g": 2, "4B2i": 2, "4B2d": 2, "5": 2}
 WORKLOAD_NAMES = {
     "1": "tiny fp32: R=1 P=256 B=4 L=2 4q/1kv D=64",
     "2": "GR semantic-ID decode: R=8 P=1024 B=128 L=3 16q/4kv D=128 bf16",
     "3": "wide beam: R=4 P=2048 B=512 L=1-3 32q/8kv D=128 bf16",
     "4A": "prefix-homogeneous: 4 prefixes x 16 seqs P=4096 +512 unique, 32q/8kv D=128 bf16",
     "4B": "prefix-heterogeneous: 64 prefixes P=4096 +512 unique, 32q/8kv D=128 bf16",
+    "4B2g": "64 single-sequence requests on 4 aliased prefixes, grouped order, P=4096 +512 unique, 32q/8kv D=128 bf16",
+    "4B2i": "64 single-sequence requests on 4 aliased prefixes, interleaved order, P=4096 +512 unique, 32q/8kv D=128 bf16",
+    "4B2d": "as 4B2g with one request on a private prefix copy (one divergent request), 32q/8kv D=128 bf16",
     "5": "long history: R=16 P=16384 B=256 L=8 64q/8kv D=128 bf16",
 }
 
@@ -60,7 +63,9 @@ def _cfg_key(s):
 def algorithmic(w):
     """Algorithmic bytes / flops of one decode call on workload w."""
     e = w.elem_bytes
-    kv_tokens = int(sum(int(w.prefix_len[r]) + w.B * int(w.unshared_len[r]) for r in range(w.R)))
+    # prompt rows once per distinct physical range (requests may alias one prefix)
+    prompt_tokens = sum(p for (o, p) in {(int(w.prefix_off[r]), int(w.prefix_len[r])) for r in range(w.R)})
+    kv_tokens = prompt_tokens + int(sum(w.B * int(w.unshared_len[r]) for r in range(w.R)))
     unique_kv = kv_tokens * w.Hkv * w.D * 2 * e
     q = w.N_b * w.Hq * w.D * e
     out = w.N_b * w.Hq * (w.D + 1) * 4

@@ -204,10 +204,15 @@ def make_workload(name: str, *, R: int, B: int, Hq: int, Hkv: int, D: int,
 # ----------------------------------------------------------------------------
 
 CONFIG_IDS = (1, 2, 3, "4A", "4B", 5)
+# Variants of config 4B (same values): the 64 single-sequence requests read
+# the 4 physical prefixes of 4A through aliased offsets, in grouped or
+# interleaved request order, or grouped with one request reading a private
+# copy of its prefix (one divergent request).
+CONFIG4_VARIANTS = ("4B2g", "4B2i", "4B2d")
 
 
 def _cfg_seed_id(cfg) -> int:
-    return {1: 1, 2: 2, 3: 3, "4A": 4, "4B": 4, 5: 5}[cfg]
+    return {1: 1, 2: 2, 3: 3, "4A": 4, "4B": 4, "4B2g": 4, "4B2i": 4, "4B2d": 4, 5: 5}[cfg]
 
 
 def config(cfg, layer: int = 0, *, unscaled: bool = False) -> Workload:
@@ -237,6 +242,11 @@ def config(cfg, layer: int = 0, *, unscaled: bool = False) -> Workload:
     if cfg == "4B":
         a = config("4A", layer, unscaled=unscaled)
         return as_distinct_prefixes(a, "cfg4B_prefix_heterogeneous")
+    if cfg in CONFIG4_VARIANTS:
+        a = config("4A", layer, unscaled=unscaled)
+        order = "interleaved" if cfg == "4B2i" else "grouped"
+        return as_aliased_prefixes(a, f"cfg{cfg}_prefix_aliased_{order}", order=order,
+                                   divergent=(cfg == "4B2d"))
     if cfg == 5:
         std = 1.0 if unscaled else 1.0 / np.sqrt(128.0)
         return make_workload("cfg5_long_history", R=16, B=256, Hq=64, Hkv=8, D=128,
@@ -272,6 +282,49 @@ def as_distinct_prefixes(w: Workload, name: str) -> Workload:
                     parents=np.zeros_like(w.parents),
                     slot_base=np.arange(N_b, dtype=np.int64) * T_max,
                     num_slots=N_b * T_max, meta=dict(w.meta, derived_from=w.name))
+
+
+def as_aliased_prefixes(w: Workload, name: str, order: str = "grouped",
+                        divergent: bool = False) -> Workload:
+    """Re-express each beam of ``w`` as its own request with beam width 1,
+    every request of a group reading the group's one physical prefix (the
+    prompt offsets alias).
+
+    order "grouped": request n is sequence n (a group's requests are
+    consecutive); "interleaved": request n belongs to group n % R, so
+    consecutive requests read different prefixes. divergent: request 0 reads
+    a private physical copy of its prefix instead. Values are unchanged, so
+    request n's output equals that of sequence meta["seq_of_request"][n] of
+    ``w``. Requires identity parents.
+    """
+    B, R = w.B, w.R
+    N_b = w.N_b
+    n = np.arange(N_b)
+    if order == "grouped":
+        seq = n
+    elif order == "interleaved":
+        seq = (n % R) * B + n // R
+    else:
+        raise ValueError(f"unknown order {order!r}")
+    grp = seq // B
+    P = w.prefix_len[grp].astype(np.int32)
+    off = w.prefix_off[grp].astype(np.int64)
+    ks, vs = w.k_shared, w.v_shared
+    if divergent:
+        o0, p0 = int(off[0]), int(P[0])
+        off = off.copy()
+        off[0] = ks.shape[1]
+        ks = np.concatenate([ks, ks[:, o0:o0 + p0]], axis=1)
+        vs = np.concatenate([vs, vs[:, o0:o0 + p0]], axis=1)
+    T_max = w.T_max
+    return Workload(name=name, dtype=w.dtype, R=N_b, B=1, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
+                    prefix_len=P, prefix_off=off,
+                    unshared_len=w.unshared_len[grp].astype(np.int32), T_max=T_max, scale=w.scale,
+                    q=w.q[seq], k_shared=ks, v_shared=vs, k_new=w.k_new[:, seq], v_new=w.v_new[:, seq],
+                    parents=np.zeros_like(w.parents),
+                    slot_base=np.arange(N_b, dtype=np.int64) * T_max,
+                    num_slots=N_b * T_max,
+                    meta=dict(w.meta, derived_from=w.name, seq_of_request=seq.tolist()))
 
 
 @dataclass

@@ -70,7 +70,7 @@ def test_config1_full():
             "config 1")
 
 
-@pytest.mark.parametrize("cfg", [2, 3, "4A", "4B", 5])
+@pytest.mark.parametrize("cfg", [2, 3, "4A", "4B", "4B2g", "4B2i", "4B2d", 5])
 def test_config_sampled(cfg):
     run_cfg(cfg)
 
@@ -84,3 +84,14 @@ def test_config4_homogeneous_equals_heterogeneous():
     _, oa_, la, _ = run_cfg("4A", k=8)
     _, ob_, lb, _ = run_cfg("4B", k=8)
     compare(oa_, ob_, la, lb, "bf16", "4A vs 4B")
+
+
+@pytest.mark.parametrize("cfg", ["4B2i", "4B2d"])
+def test_config4_homogeneous_equals_aliased(cfg):
+    """Aliased prompt offsets (interleaved order; one private copy) read the
+    same values as the homogeneous batch: outputs match it row for row,
+    permuted to the aliased request order."""
+    _, oa_, la, _ = run_cfg("4A", k=8)
+    w, ob_, lb, _ = run_cfg(cfg, k=8)
+    seq = np.array(w.meta["seq_of_request"])
+    compare(ob_, oa_[seq], lb, la[seq], "bf16", f"4A vs {cfg}")

@@ -284,3 +284,23 @@ def test_prefix_homogeneous_equals_distinct_prefixes():
     Ob, Lb = oa.attention(b)
     np.testing.assert_allclose(Oa, Ob, atol=1e-13)
     np.testing.assert_allclose(La, Lb, atol=1e-13)
+
+
+@pytest.mark.parametrize("order,divergent", [("grouped", False), ("interleaved", False), ("grouped", True)])
+def test_prefix_homogeneous_equals_aliased_prefixes(order, divergent):
+    """Aliased prompt offsets (one physical prefix per group, or one private
+    copy) change where the prompt is read, not what: request n's attention
+    equals that of its sequence in the homogeneous layout."""
+    a = make_workload("4a-mini", R=3, B=4, Hq=4, Hkv=2, D=16, prefix_len=[21, 9, 30], unshared_len=4,
+                      seed_key=(111, 0), parent_dist="identity")
+    b = inputs.as_aliased_prefixes(a, "4b2-mini", order=order, divergent=divergent)
+    seq = np.array(b.meta["seq_of_request"])
+    assert sorted(seq.tolist()) == list(range(a.N_b))
+    if order == "interleaved":
+        assert len(set(int(o) for o in b.prefix_off[:a.R])) == a.R  # consecutive requests, distinct prefixes
+    if divergent:
+        assert int(b.prefix_off[0]) >= a.k_shared.shape[1]
+    Oa, La = oa.attention(a)
+    Ob, Lb = oa.attention(b)
+    np.testing.assert_allclose(Ob, Oa.reshape(a.N_b, a.Hq, a.D)[seq].reshape(Ob.shape), atol=1e-13)
+    np.testing.assert_allclose(Lb, La.reshape(a.N_b, a.Hq)[seq].reshape(Lb.shape), atol=1e-13)
