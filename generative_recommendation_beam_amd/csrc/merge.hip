@@ -67,18 +67,26 @@ __global__ __launch_bounds__(kMergeThreads) void merge_parts_kernel(int64_t rows
   const int64_t row = gid / tpr;
   const int c = (int)(gid - row * tpr);
   if (row >= rows) return;
+  // The loops are unrolled so that several parts' loads are in flight at once
+  // (one round trip per few parts instead of one per part); a part with no
+  // keys (lse = -inf) is selected away rather than branched around.
   float m = neg_inf();
+#pragma unroll 8
   for (int i = 0; i < parts; ++i) m = fmaxf(m, plse[(int64_t)i * rows + row]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float lse = neg_inf();
   if (m != neg_inf()) {
     float s = 0.f;
+#pragma unroll 4
     for (int i = 0; i < parts; ++i) {
       const float li = plse[(int64_t)i * rows + row];
-      if (li == neg_inf()) continue;
-      const float w = exp2_approx((li - m) * kLog2e);
       const float4 v = reinterpret_cast<const float4*>(po + ((int64_t)i * rows + row) * D)[c];
-      acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+      const bool on = li != neg_inf();
+      const float w = on ? exp2_approx((li - m) * kLog2e) : 0.f;
+      acc.x += on ? w * v.x : 0.f;
+      acc.y += on ? w * v.y : 0.f;
+      acc.z += on ? w * v.z : 0.f;
+      acc.w += on ? w * v.w : 0.f;
       s += w;
     }
     const float inv = 1.0f / s;
