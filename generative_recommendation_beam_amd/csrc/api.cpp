@@ -17,15 +17,21 @@ constexpr int kMaxBeamWidth = 16384;   // one request's table chunk must fit in 
 constexpr int kTargetWaves = 2048;     // vector path: resident waves to cover 256 CUs
 // MFMA path: split the prompt only until this many workgroups exist. Measured
 // on MI355X, a split's partial write and in-kernel merge cost more than the
-// extra parallelism returns once half the CUs hold a workgroup.
+// extra parallelism returns once half the CUs hold a workgroup. When the
+// generated tokens go to their own launch (long tails), the prompt splits
+// join that launch's merge instead, and one workgroup per CU measured best
+// (4096-token prompts, 512-token tails: 70.3 -> 67.1 us per call).
 constexpr int kTargetMfmaBlocks = 128;
+constexpr int kTargetMfmaBlocksLongTail = 256;
 constexpr int kMinSplitKeys = 256;     // MFMA path: never split the prompt finer than this
 // Vector path: a wave walks its keys a few rows per memory round trip, so a
 // short prompt over few waves is latency-bound; splits down to this many keys
 // (merged by one more launch) pay off there.
 constexpr int kMinSplitKeysValu = 64;
 constexpr int kFuseMaxUnshared = 16;   // T_max up to this: Non-Shared part in the epilogue
-constexpr int kUnsharedChunk = 64;     // generated tokens per Non-Shared split
+// Generated tokens per Non-Shared split. Measured on MI355X with 512-token
+// tails: 128 beats 64 (fewer partial rows to merge, half the wave starts).
+constexpr int kUnsharedChunk = 128;
 constexpr int kMfmaMinRows = 16;       // fewer query rows per (r,h): vector path
 constexpr int kKeyGroupMinKeys = 512;  // automatic key groups only for prompts this long
 constexpr int kNumCUs = 256;           // MI355X compute units
@@ -121,7 +127,8 @@ Plan make_plan(const xattn_dims* d, int which) {
       p.waves = rows / 32 * kg;
       p.row_tiles = (int)cdiv(M, rows);
       base_units = (int64_t)d->num_requests * d->num_kv_heads * p.row_tiles;  // workgroups
-      target_units = kTargetMfmaBlocks;
+      const bool long_tail = which == 2 && (d->unshared_splits > 0 || T > kFuseMaxUnshared);
+      target_units = long_tail ? kTargetMfmaBlocksLongTail : kTargetMfmaBlocks;
     } else {
       p.waves = 1;
       p.row_tiles = 1;
@@ -146,7 +153,7 @@ Plan make_plan(const xattn_dims* d, int which) {
     if (which == 1) {
       // Non-Shared stage alone: split only long generated tails.
       const int s = d->unshared_splits > 0 ? d->unshared_splits
-                                           : (T > 4 * kUnsharedChunk ? (int)cdiv(T, kUnsharedChunk) : 1);
+                                           : (T > 2 * kUnsharedChunk ? (int)cdiv(T, kUnsharedChunk) : 1);
       p.u_chunk = (int)cdiv(T, s);
       p.u_splits = (int)cdiv(T, p.u_chunk);
     } else {

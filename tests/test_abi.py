@@ -123,6 +123,11 @@ def test_plan_introspection(L):
     d2 = dims(R=4, B=16, Hq=32, Hkv=8, max_prefix_len=4096, max_unshared_len=512)
     p2 = xattn.get_plan(d2, 2)
     assert p2["unshared_splits"] > 0 and p2["partials"] == p2["prefix_splits"] + p2["unshared_splits"]
+    assert p2["unshared_chunk"] == 128 and p2["unshared_splits"] == 4  # 128 generated tokens per split
+    # with the tail in its own launch, the prompt splits until every CU holds a workgroup
+    assert p2["prefix_splits"] == 8 and p2["prefix_chunk"] == 512
+    p2s = xattn.get_plan(d2, 1)   # the Non-Shared stage alone splits a 512-token tail the same way
+    assert p2s["unshared_splits"] == 4 and p2s["partials"] == 4
     p3 = xattn.get_plan(dims(dtype=xattn.XATTN_F32), 2)
     assert p3["mfma"] == 0
     # the vector path splits a short prompt over few waves down to 64 keys
