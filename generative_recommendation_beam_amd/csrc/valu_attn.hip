@@ -2,8 +2,7 @@
 //
 // Used for the Non-Shared stage (xGR page, section 2.1 xAttention: each beam
 // attends to its own generated tokens, gathered through its slot-table row
-// from the token-granular pool), for the fp32 path, and for the Shared stage
-// when a (request, kv head) has too few query rows to fill an MFMA tile.
+// from the token-granular pool) and for the fp32 path.
 // The Non-Shared work is bandwidth-bound and tiny per beam: a GEMV, not a
 // contraction worth the matrix cores.
 //

@@ -76,7 +76,9 @@ typedef struct {
   int32_t num_q_heads;      /* H_q >= 1, a multiple of num_kv_heads */
   int32_t num_kv_heads;     /* H_kv >= 1 */
   int32_t head_dim;         /* D: 64 or 128 */
-  int32_t max_prefix_len;   /* >= every prefix_len[r]; sizes the prefix split plan */
+  int32_t max_prefix_len;   /* >= every prefix_len[r]; sizes the prefix split plan.
+                               max_prefix_len * head_dim * element bytes must stay
+                               below 2^31 (else XATTN_ERR_UNSUPPORTED) */
   int32_t max_unshared_len; /* T_max >= 1: slot-table row stride, >= every unshared_len[r] */
   int32_t dtype;            /* xattn_dtype of q and every K/V buffer */
   int64_t num_slots;        /* capacity of k_pool / v_pool in tokens */

@@ -70,6 +70,8 @@ def _decode(d, ws=None, nbytes=0, **over):
     (dict(key_groups=4, D=64), xattn.XATTN_ERR_UNSUPPORTED),
     (dict(key_groups=4, rows_per_block=128), xattn.XATTN_ERR_UNSUPPORTED),
     (dict(rows_per_block=96), xattn.XATTN_ERR_INVALID_ARG),
+    (dict(max_prefix_len=1 << 23), xattn.XATTN_ERR_UNSUPPORTED),   # prompt bytes reach 2^31
+    (dict(max_prefix_len=1 << 22, dtype=xattn.XATTN_F32), xattn.XATTN_ERR_UNSUPPORTED),
 ])
 def test_invalid_dims_rejected(L, over, code):
     assert _decode(dims(**over)) == code
@@ -135,6 +137,12 @@ def test_plan_introspection(L):
     p4 = xattn.get_plan(dims(R=1, B=4, Hq=4, Hkv=1, D=64, max_prefix_len=256, max_unshared_len=2,
                              dtype=xattn.XATTN_F32), 2)
     assert p4["mfma"] == 0 and p4["prefix_splits"] == 4 and p4["prefix_chunk"] == 64
+    # bf16 always takes the matrix cores: one beam's 4 query rows in a 32-row
+    # tile, whose K/V tiles four waves share (long prompts, head dim 128)
+    p6 = xattn.get_plan(dims(R=64, B=1, Hq=32, Hkv=8, max_prefix_len=4096, max_unshared_len=512), 2)
+    assert p6["mfma"] == 1 and p6["rows_per_block"] == 32 and p6["key_groups"] == 4
+    p7 = xattn.get_plan(dims(R=2, B=1, Hq=4, Hkv=1, D=64, max_prefix_len=300, max_unshared_len=3), 2)
+    assert p7["mfma"] == 1 and p7["rows_per_block"] == 32 and p7["key_groups"] == 1
     # enough workgroups already: one key group
     p5 = xattn.get_plan(dims(R=16, B=256, Hq=64, Hkv=8, max_prefix_len=16384, max_unshared_len=8), 2)
     assert p5["key_groups"] == 1 and p5["rows_per_block"] == 128
