@@ -26,6 +26,23 @@ namespace {
 
 constexpr int kValuWaves = 4;
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over a key slot's 16 lanes (one DPP row), every lane getting the same
+// bits: the butterfly over lane distances 8, 4, 2, 1, with the first two as
+// row rotations (equal to the exchanges once the partial sums are symmetric)
+// and the last two as quad permutations. Register-to-register, no LDS.
+__device__ __forceinline__ float slot_sum(float x) {
+  x += dpp_f32<0x128>(x);  // row_ror:8 (lane i ^ 8)
+  x += dpp_f32<0x124>(x);  // row_ror:4 (x now symmetric under i ^ 8)
+  x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1] (lane i ^ 2)
+  x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2] (lane i ^ 1)
+  return x;
+}
+
 template <typename T, int D, int NG>
 struct ValuState {
   static constexpr int EPL = D / 16;
@@ -56,10 +73,7 @@ struct ValuState {
       s[g] = a;
     }
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-#pragma unroll
-      for (int g = 0; g < NG; ++g) s[g] += __shfl_xor(s[g], off);
-    }
+    for (int g = 0; g < NG; ++g) s[g] = slot_sum(s[g]);
     if (valid) {
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
