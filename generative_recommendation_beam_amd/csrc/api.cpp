@@ -169,8 +169,7 @@ Plan make_plan(const xattn_dims* d, int which) {
       p.u_splits = (int)cdiv(T, p.u_chunk);
     } else {
       // decode: fuse into the prompt pass when short and not forced apart
-      const bool fuse = d->unshared_splits == 0 && T <= kFuseMaxUnshared &&
-                        (p.mfma || p.p_splits == 1);
+      const bool fuse = d->unshared_splits == 0 && T <= kFuseMaxUnshared;
       if (!fuse) {
         const int s = d->unshared_splits > 0 ? d->unshared_splits : (int)cdiv(T, kUnsharedChunk);
         p.u_chunk = (int)cdiv(T, s);

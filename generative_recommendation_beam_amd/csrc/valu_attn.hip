@@ -43,6 +43,20 @@ __device__ __forceinline__ float slot_sum(float x) {
   return x;
 }
 
+// The value of lane i ^ LM (LM = 16 or 32) through the gfx950 lane swaps,
+// register to register. The whole wavefront must be active.
+template <int LM>
+__device__ __forceinline__ float xor_far(float x, int lane) {
+  const uint32_t v = __builtin_bit_cast(uint32_t, x);
+  if constexpr (LM == 16) {  // odd 16-lane rows of one copy swapped with even rows of the other
+    const auto w = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return __builtin_bit_cast(float, (lane & 16) ? w[0] : w[1]);
+  } else {  // upper 32 lanes of one copy swapped with the lower 32 of the other
+    const auto w = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __builtin_bit_cast(float, (lane & 32) ? w[0] : w[1]);
+  }
+}
+
 template <typename T, int D, int NG>
 struct ValuState {
   static constexpr int EPL = D / 16;
@@ -89,24 +103,26 @@ struct ValuState {
   }
 
   // Combine the 4 key slots (lanes 16 and 32 apart).
-  __device__ __forceinline__ void combine_slots() {
+  __device__ __forceinline__ void combine_slots(int lane) {
+    combine_with<16>(lane);
+    combine_with<32>(lane);
+  }
+  template <int off>
+  __device__ __forceinline__ void combine_with(int lane) {
 #pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
+    for (int g = 0; g < NG; ++g) {
+      const float mo = xor_far<off>(m[g], lane);
+      const float lo = xor_far<off>(l[g], lane);
+      const float mn = fmaxf(m[g], mo);
+      const float a1 = (m[g] == neg_inf()) ? 0.f : exp2_approx(m[g] - mn);
+      const float a2 = (mo == neg_inf()) ? 0.f : exp2_approx(mo - mn);
+      l[g] = l[g] * a1 + lo * a2;
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const float mo = __shfl_xor(m[g], off);
-        const float lo = __shfl_xor(l[g], off);
-        const float mn = fmaxf(m[g], mo);
-        const float a1 = (m[g] == neg_inf()) ? 0.f : exp2_approx(m[g] - mn);
-        const float a2 = (mo == neg_inf()) ? 0.f : exp2_approx(mo - mn);
-        l[g] = l[g] * a1 + lo * a2;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const float ao = __shfl_xor(acc[g][e], off);
-          acc[g][e] = acc[g][e] * a1 + ao * a2;
-        }
-        m[g] = mn;
+      for (int e = 0; e < EPL; ++e) {
+        const float ao = xor_far<off>(acc[g][e], lane);
+        acc[g][e] = acc[g][e] * a1 + ao * a2;
       }
+      m[g] = mn;
     }
   }
 };
@@ -178,7 +194,7 @@ __global__ __launch_bounds__(kValuWaves * 64) void valu_attn_kernel(ValuArgs a, 
       for (int u = 0; u < U; ++u) st.update(kv[u], vv[u], j0 + 4 * u + slot_id < k1);
     }
   }
-  if (a.use_gen) {
+  if (a.use_gen && (!a.use_prefix || split == 0)) {  // beside a split prompt: in split 0
     const int L = a.unshared_len[r];
     int t0 = 0, t1 = L;
     if (!a.use_prefix) {
@@ -208,7 +224,7 @@ __global__ __launch_bounds__(kValuWaves * 64) void valu_attn_kernel(ValuArgs a, 
       }
     }
   }
-  st.combine_slots();
+  st.combine_slots(lane);
 
   if (slot_id != 0) return;
   const int64_t row0 = n * s.Hq + h * G + g0;
