@@ -63,6 +63,14 @@ CASES = {
                         dict(prefix_splits=3), False),
     "fallback_f32": (dict(R=2, B=4, Hq=4, Hkv=1, D=64, prefix_len=[256, 100], unshared_len=[2, 3],
                           dtype="f32"), {}, False),
+    # single-beam prompts on the matrix cores: a beam's few query rows in one
+    # 32-row tile (four key groups from 512-key prompts at head dim 128)
+    "one_beam_kg4": (dict(R=3, B=1, Hq=8, Hkv=2, D=128, prefix_len=[700, 512, 90], unshared_len=[3, 2, 1]),
+                     ONE, True),
+    "two_beams_g8": (dict(R=2, B=2, Hq=16, Hkv=2, D=128, prefix_len=[600, 300], unshared_len=[3, 1]), ONE, True),
+    "one_beam_d64": (dict(R=2, B=1, Hq=4, Hkv=1, D=64, prefix_len=[520, 33], unshared_len=[2, 2]), ONE, True),
+    "one_beam_splits": (dict(R=2, B=1, Hq=8, Hkv=2, D=128, prefix_len=[1500, 700], unshared_len=[3, 2]), {},
+                        False),
 }
 
 
