@@ -147,6 +147,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const float* bas
                                            (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff), 0x00020000);
 }
 
+// The value of lane i ^ 32, through the gfx950 lane swap (register to
+// register: an LDS permute would make the next wait on LDS reads also wait
+// for it). The whole wavefront must be active.
+__device__ __forceinline__ float xor32(float x) {
+  const auto w = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, (__lane_id() & 32) ? w[0] : w[1]);
+}
+
 // Online-softmax update for one 32-key half of a tile (S^T block `sb`, the
 // 16 scores this lane holds for its query column), followed by that half's
 // P.V MFMAs. Processing the halves separately lets the vector-ALU softmax of
@@ -168,7 +177,7 @@ __device__ __forceinline__ void half_softmax_pv(const char* buf, int vbase, f32x
 #pragma unroll
   for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sb[i]), sb[i + 1]);
   mx = fmaxf(mx, sb[15]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+  mx = fmaxf(mx, xor32(mx)) * c;
   if (__any(mx > m_run + 8.0f)) {
     const float mn = fmaxf(m_run, mx);
     const float alpha = exp2_approx(m_run - mn);
@@ -384,7 +393,7 @@ __device__ __forceinline__ void token_update(const uint4* kk, const uint2 (*vv)[
 #pragma unroll
     for (int j = 0; j < 8; ++j) dot += (float)qf[dc][j] * (float)k8[j];
   }
-  dot += __shfl_xor(dot, 32);
+  dot += xor32(dot);
   const float st = dot * c;
   if (st > m_run) {
     const float alpha = exp2_approx(m_run - st);
@@ -896,7 +905,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
       a.ulen_rw[r] = grow ? t_app + 1 : t_app;
   }
 
-  float l_tot = l_part + __shfl_xor(l_part, 32);
+  float l_tot = l_part + xor32(l_part);
   // own[j]: column block kg*NDBW + j of this wave's 32 rows, combined over
   // the key groups. Each group hands every other group the column blocks
   // that group finalizes (KG - 1 slots per block), then merges the ones it
