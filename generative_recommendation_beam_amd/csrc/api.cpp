@@ -28,6 +28,7 @@ constexpr int kMinSplitKeys = 256;     // MFMA path: never split the prompt fine
 // short prompt over few waves is latency-bound; splits down to this many keys
 // (merged by one more launch) pay off there.
 constexpr int kMinSplitKeysValu = 64;
+constexpr int kValuWgMergeMax = 8;  // the vector kernel's in-workgroup split merge, at most
 constexpr int kFuseMaxUnshared = 16;   // T_max up to this: Non-Shared part in the epilogue
 // Generated tokens per Non-Shared split. Measured on MI355X with 512-token
 // tails: 128 beats 64 (fewer partial rows to merge, half the wave starts).
@@ -183,6 +184,11 @@ Plan make_plan(const xattn_dims* d, int which) {
   // A prompt split merged in-kernel with the Non-Shared tokens as its own
   // group member needs one more partial slot.
   if (which == 2 && p.mfma && p.p_splits > 1 && p.u_splits == 0) p.parts = p.p_splits + 1;
+  // Vector path: a few prompt splits (and the short tail folded into split 0)
+  // run as the waves of one workgroup and are merged there in LDS, so the
+  // call needs no partials and no Merge launch.
+  if (!p.mfma && which != 1 && p.p_splits > 1 && p.p_splits <= kValuWgMergeMax && p.u_splits == 0)
+    p.parts = 0;
   // Two LDS stages measured best on every workload (four fit only one
   // workgroup per CU and push accumulators into AGPRs); four on request.
   p.stages = p.mfma ? (d->pipeline_stages ? d->pipeline_stages : 2) : 0;

@@ -25,6 +25,7 @@ namespace xattn {
 namespace {
 
 constexpr int kValuWaves = 4;
+constexpr int kValuWgMax = 8;  // splits merged inside one workgroup (one wave each), at most
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -127,9 +128,12 @@ struct ValuState {
   }
 };
 
-template <typename T, int D, int NG>
-__global__ __launch_bounds__(kValuWaves * 64) void valu_attn_kernel(ValuArgs a, int64_t n_units,
-                                                                    int ngroups) {
+// WGM: the splits of one (beam, kv head, head group) are the waves of one
+// workgroup (wave w = split w) and are merged there, in split order, into the
+// final output; otherwise kValuWaves consecutive units per workgroup.
+template <typename T, int D, int NG, bool WGM>
+__global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_attn_kernel(
+    ValuArgs a, int64_t n_units, int ngroups) {
   constexpr int EPL = D / 16;
   // Steps per batch: 64 dwords of K/V rows in flight per lane at most (32
   // with 8 query heads, whose state takes twice the registers), 8 steps at
@@ -138,7 +142,7 @@ __global__ __launch_bounds__(kValuWaves * 64) void valu_attn_kernel(ValuArgs a, 
   constexpr int BUF_DW = NG >= 8 ? 32 : 64;
   constexpr int U = BUF_DW / STEP_DW < 8 ? BUF_DW / STEP_DW : 8;
   const int lane = threadIdx.x & 63;
-  const int64_t unit = (int64_t)blockIdx.x * kValuWaves + (threadIdx.x >> 6);
+  const int64_t unit = (int64_t)blockIdx.x * (WGM ? a.splits : kValuWaves) + (threadIdx.x >> 6);
   if (unit >= n_units) return;  // uniform per wavefront
   const Shape& s = a.s;
   int64_t u = unit;
@@ -226,6 +230,40 @@ __global__ __launch_bounds__(kValuWaves * 64) void valu_attn_kernel(ValuArgs a, 
   }
   st.combine_slots(lane);
 
+  if constexpr (WGM) {  // the grid holds exactly n_units waves: all reach the barrier
+    __shared__ float s_ml[kValuWgMax][NG][2];
+    __shared__ float s_acc[kValuWgMax][NG][D];
+    if (slot_id == 0) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s_acc[split][g][dl * EPL + e] = st.acc[g][e];
+        if (dl == 0) {
+          s_ml[split][g][0] = st.m[g];
+          s_ml[split][g][1] = st.l[g];
+        }
+      }
+    }
+    __syncthreads();
+    if (split != 0) return;  // uniform per wavefront
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float mt = neg_inf();
+      for (int w = 0; w < a.splits; ++w) mt = fmaxf(mt, s_ml[w][g][0]);
+      float lt = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) st.acc[g][e] = 0.f;
+      for (int w = 0; w < a.splits; ++w) {
+        const float mw = s_ml[w][g][0];
+        const float sc = mw == neg_inf() ? 0.f : exp2_approx(mw - mt);
+        lt += s_ml[w][g][1] * sc;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) st.acc[g][e] += s_acc[w][g][dl * EPL + e] * sc;
+      }
+      st.m[g] = mt;
+      st.l[g] = lt;
+    }
+  }
   if (slot_id != 0) return;
   const int64_t row0 = n * s.Hq + h * G + g0;
   float* ob = a.out.o;
@@ -259,13 +297,26 @@ hipError_t launch_typed(const ValuArgs& a, hipStream_t st) {
   const int ngroups = (G + NG - 1) / NG;
   const int64_t units = N_b * a.s.Hkv * ngroups * a.splits;
   if (units == 0) return hipSuccess;
-  const int64_t blocks = (units + kValuWaves - 1) / kValuWaves;
-  dim3 grid((unsigned)blocks), block(kValuWaves * 64);
+  // Splits written straight to the final output are merged in their workgroup.
+  const bool wgm = a.splits > 1 && a.out.part_stride == 0;
+  if (wgm && a.splits > kValuWgMax) return hipErrorInvalidValue;
+  const int wpb = wgm ? a.splits : kValuWaves;
+  const int64_t blocks = (units + wpb - 1) / wpb;
+  dim3 grid((unsigned)blocks), block(wpb * 64);
+  if (wgm) {
+    switch (NG) {
+      case 1: hipLaunchKernelGGL((valu_attn_kernel<T, D, 1, true>), grid, block, 0, st, a, units, ngroups); break;
+      case 2: hipLaunchKernelGGL((valu_attn_kernel<T, D, 2, true>), grid, block, 0, st, a, units, ngroups); break;
+      case 4: hipLaunchKernelGGL((valu_attn_kernel<T, D, 4, true>), grid, block, 0, st, a, units, ngroups); break;
+      default: hipLaunchKernelGGL((valu_attn_kernel<T, D, 8, true>), grid, block, 0, st, a, units, ngroups); break;
+    }
+    return hipGetLastError();
+  }
   switch (NG) {
-    case 1: hipLaunchKernelGGL((valu_attn_kernel<T, D, 1>), grid, block, 0, st, a, units, ngroups); break;
-    case 2: hipLaunchKernelGGL((valu_attn_kernel<T, D, 2>), grid, block, 0, st, a, units, ngroups); break;
-    case 4: hipLaunchKernelGGL((valu_attn_kernel<T, D, 4>), grid, block, 0, st, a, units, ngroups); break;
-    default: hipLaunchKernelGGL((valu_attn_kernel<T, D, 8>), grid, block, 0, st, a, units, ngroups); break;
+    case 1: hipLaunchKernelGGL((valu_attn_kernel<T, D, 1, false>), grid, block, 0, st, a, units, ngroups); break;
+    case 2: hipLaunchKernelGGL((valu_attn_kernel<T, D, 2, false>), grid, block, 0, st, a, units, ngroups); break;
+    case 4: hipLaunchKernelGGL((valu_attn_kernel<T, D, 4, false>), grid, block, 0, st, a, units, ngroups); break;
+    default: hipLaunchKernelGGL((valu_attn_kernel<T, D, 8, false>), grid, block, 0, st, a, units, ngroups); break;
   }
   return hipGetLastError();
 }

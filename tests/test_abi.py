@@ -137,8 +137,11 @@ def test_plan_introspection(L):
     p4 = xattn.get_plan(dims(R=1, B=4, Hq=4, Hkv=1, D=64, max_prefix_len=256, max_unshared_len=2,
                              dtype=xattn.XATTN_F32), 2)
     assert p4["mfma"] == 0 and p4["prefix_splits"] == 4 and p4["prefix_chunk"] == 64
-    # its short generated tail rides in prompt split 0: no launch of its own
-    assert p4["unshared_splits"] == 0 and p4["partials"] == 4
+    # its short generated tail rides in prompt split 0, and the 4 splits of a
+    # (beam, kv head) are merged inside their workgroup: one launch, no workspace
+    assert p4["unshared_splits"] == 0 and p4["partials"] == 0 and p4["launches"] == 1
+    assert xattn.get_plan(dims(R=1, B=1, Hq=4, Hkv=1, D=64, max_prefix_len=4096, max_unshared_len=2,
+                               dtype=xattn.XATTN_F32), 2)["partials"] > 8   # too many splits: Merge launch
     # bf16 always takes the matrix cores: one beam's 4 query rows in a 32-row
     # tile, whose K/V tiles four waves share (long prompts, head dim 128)
     p6 = xattn.get_plan(dims(R=64, B=1, Hq=32, Hkv=8, max_prefix_len=4096, max_unshared_len=512), 2)
