@@ -87,6 +87,24 @@ def test_decode_forced_splits(splits):
     compare(o, O, lse, L, "bf16", f"decode splits={splits} plan={plan}")
 
 
+@pytest.mark.parametrize("shape,ps", [
+    # 8 head-group query rows, 8 splits merged in one workgroup; the shorter
+    # prompt leaves most of its splits empty
+    (dict(R=2, B=3, Hq=8, Hkv=1, D=128, prefix_len=[500, 40], unshared_len=[3, 1]), 8),
+    # 3 query heads per kv head (one masked group of 8), an empty prompt, no tail
+    (dict(R=3, B=2, Hq=3, Hkv=1, D=64, prefix_len=[300, 0, 129], unshared_len=[2, 2, 0], T_max=3), 5),
+    # one query head per kv head; 9 splits: partials and a Merge launch instead
+    (dict(R=2, B=5, Hq=2, Hkv=2, D=64, prefix_len=[1100, 333], unshared_len=[1, 4]), 9),
+])
+def test_f32_vector_splits(shape, ps):
+    w = make_workload("f32_splits", dtype="f32", seed_key=(305, ps), parent_dist="uniform", **shape)
+    d, o, lse = run_decode(w, prefix_splits=ps)
+    plan = xattn.get_plan(d.dims, 2)
+    assert plan["mfma"] == 0 and plan["prefix_splits"] == ps and (plan["partials"] == 0) == (ps <= 8), plan
+    O, L = oa.attention(w)
+    compare(o, O, lse, L, "f32", f"f32 vector splits={ps} plan={plan}")
+
+
 KG_CASES = ["ragged_small_bf16", "mfma_multi_tile", "d64_bf16", "g8_bf16", "g16_bf16", "g6_bf16", "no_prefix_bf16",
             "tb_mix_bf16",
             "no_gen_bf16", "long_gen_bf16"]
