@@ -92,13 +92,22 @@ struct ValuState {
     if (valid) {
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        const float mn = fmaxf(m[g], s[g]);
-        const float alpha = exp2_approx(m[g] - mn);  // m = -inf -> 0
-        const float p = exp2_approx(s[g] - mn);
-        l[g] = l[g] * alpha + p;
+        // Lazy rescale: the reference maximum moves only when a score passes
+        // it by more than 8 (log2 units), so every weight stays below 2^8 and
+        // most steps skip the accumulator rescale. The 16 lanes of a key slot
+        // hold the same bits, so the choice is the same across them.
+        if (__any(s[g] > m[g] + 8.0f)) {
+          const float mn = fmaxf(m[g], s[g]);
+          const float alpha = exp2_approx(m[g] - mn);  // m = -inf -> 0
+          l[g] *= alpha;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] = acc[g][e] * alpha + p * vv[e];
-        m[g] = mn;
+          for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+          m[g] = mn;
+        }
+        const float p = exp2_approx(s[g] - m[g]);
+        l[g] += p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] += p * vv[e];
       }
     }
   }
