@@ -58,10 +58,63 @@ __device__ __forceinline__ float xor_far(float x, int lane) {
   }
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// One lane's share (EPL elements) of a key or query row as the score needs
+// it: bf16 rows stay as loaded, two elements per dword, for the packed bf16
+// dot product (products exact, sums in fp32); fp32 rows as floats.
+template <typename T, int EPL>
+struct KRow;
+template <int EPL>
+struct KRow<uint16_t, EPL> {
+  uint32_t w[EPL / 2];
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    if constexpr (EPL == 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p);
+      w[0] = v.x;
+      w[1] = v.y;
+      w[2] = v.z;
+      w[3] = v.w;
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      w[0] = v.x;
+      w[1] = v.y;
+    }
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < EPL / 2; ++i) w[i] = 0u;
+  }
+  __device__ __forceinline__ float dot(const KRow& k) const {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL / 2; ++i)
+      a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]), __builtin_bit_cast(bf16x2_t, k.w[i]), a,
+                                          false);
+    return a;
+  }
+};
+template <int EPL>
+struct KRow<float, EPL> {
+  float f[EPL];
+  __device__ __forceinline__ void load(const float* p) { Load<float, EPL>::run(p, f); }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) f[e] = 0.f;
+  }
+  __device__ __forceinline__ float dot(const KRow& k) const {
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) a += f[e] * k.f[e];
+    return a;
+  }
+};
+
 template <typename T, int D, int NG>
 struct ValuState {
   static constexpr int EPL = D / 16;
-  float q[NG][EPL];
+  KRow<T, EPL> q[NG];  // bf16: as loaded; fp32: pre-scaled by scale_log2
+  float qscale;        // applied to each bf16 score (the fp32 q carries it)
   float m[NG], l[NG];
   float acc[NG][EPL];
 
@@ -78,15 +131,10 @@ struct ValuState {
   // One step over the 4 keys held by the 4 slots: kv / vv are this lane's
   // D/16 elements of its slot's key and value rows; `valid` is uniform per
   // slot.
-  __device__ __forceinline__ void update(const float* kv, const float* vv, bool valid) {
+  __device__ __forceinline__ void update(const KRow<T, EPL>& kv, const float* vv, bool valid) {
     float s[NG];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      float a = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) a += q[g][e] * kv[e];
-      s[g] = a;
-    }
+    for (int g = 0; g < NG; ++g) s[g] = sizeof(T) == 2 ? q[g].dot(kv) * qscale : q[g].dot(kv);
 #pragma unroll
     for (int g = 0; g < NG; ++g) s[g] = slot_sum(s[g]);
     if (valid) {
@@ -172,17 +220,17 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
   st.init();
   {
     const T* qb = static_cast<const T*>(a.q) + ((n * s.Hq) + h * G + g0) * (int64_t)D + dl * EPL;
+    st.qscale = s.scale_log2;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      float tmp[EPL];
-      if (g < ng) {
-        Load<T, EPL>::run(qb + (int64_t)g * D, tmp);
-      } else {
+      if (g < ng)
+        st.q[g].load(qb + (int64_t)g * D);
+      else
+        st.q[g].zero();
+      if constexpr (sizeof(T) == 4) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) tmp[e] = 0.f;
+        for (int e = 0; e < EPL; ++e) st.q[g].f[e] *= s.scale_log2;
       }
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) st.q[g][e] = tmp[e] * s.scale_log2;
     }
   }
 
@@ -196,11 +244,12 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
     const T* kb = static_cast<const T*>(a.k_shared) + ((int64_t)h * s.n_ptok + a.prefix_off[r]) * D + dl * EPL;
     const T* vb = static_cast<const T*>(a.v_shared) + ((int64_t)h * s.n_ptok + a.prefix_off[r]) * D + dl * EPL;
     for (int j0 = k0; j0 < k1; j0 += 4 * U) {
-      float kv[U][EPL], vv[U][EPL];
+      KRow<T, EPL> kv[U];
+      float vv[U][EPL];
 #pragma unroll
       for (int u = 0; u < U; ++u) {  // keys past k1 read row k1-1 and are skipped
         const int64_t jj = min(j0 + 4 * u + slot_id, k1 - 1);
-        Load<T, EPL>::run(kb + jj * D, kv[u]);
+        kv[u].load(kb + jj * D);
         Load<T, EPL>::run(vb + jj * D, vv[u]);
       }
 #pragma unroll
@@ -224,10 +273,11 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
 #pragma unroll
       for (int u = 0; u < U; ++u) slot[u] = trow[min(t0 + 4 * u + slot_id, t1 - 1)];
       for (int j0 = t0; j0 < t1; j0 += 4 * U) {
-        float kv[U][EPL], vv[U][EPL];
+        KRow<T, EPL> kv[U];
+        float vv[U][EPL];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          Load<T, EPL>::run(kp + slot[u] * tok_stride, kv[u]);
+          kv[u].load(kp + slot[u] * tok_stride);
           Load<T, EPL>::run(vp + slot[u] * tok_stride, vv[u]);
         }
 #pragma unroll
