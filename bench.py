@@ -9,29 +9,39 @@ launch), on n_layers distinct layer buffers (distinct Q, prompt KV,
 Non-Shared pool, slot tables and lengths per layer, so the working set
 defeats the 256 MB Infinity Cache). By default the whole step is one
 captured HIP graph (xattn_step_graph_*), launched once per step; --eager
-launches every call from the host instead. Inputs are synthetic, shaped like
-the GR semantic-ID workload by default (8 requests, 1024-token user-history
-prompt, beam width 128, 3 generated tokens, 16 q / 4 kv heads, head dim 128,
-bf16), and resident in HBM before the timed region; the cache holds every
-earlier step, and each timed step restores the lengths (one small device
-copy) and appends the last step's tokens again, so every step does the same
-work.
+launches every call from the host instead.
+
+The default workload is the long-history one (16 requests, 16384-token
+user-history prompt, beam width 256, 8 generated tokens, 64 q / 8 kv heads,
+head dim 128, bf16: about 1 GB of prompt KV per layer), the largest
+configuration that fits one GPU; the GR semantic-ID workload (8 requests,
+1024-token prompt, beam width 128, 3 tokens, 16 q / 4 kv heads) is measured
+in the same run as an extra block. Inputs are synthetic, resident in HBM
+before the timed region; the cache holds every earlier step, and each timed
+step restores the lengths (one small device copy) and appends the last
+step's tokens again, so every step does the same work.
 
 Prints ONE JSON line. Metric: beams * layer-steps per second, plus achieved
 HBM bandwidth on algorithmic bytes (unique KV: prompt KV once per request,
 generated KV once per beam; plus the append's new rows and table cells) and
 the roofline of the dominant kernel (the fused append + decode launch). Its
-per-launch duration comes from HIP events: around every call of the timed
-steps with --eager; in graph mode, around K launches of a graph of every
-layer's call, right after the timed steps, each after the lengths are
-restored (events cannot be recorded inside a captured graph on the runtime
-PyTorch ships).
+per-launch duration comes from HIP events on the launch stream: around every
+call of the timed steps with --eager; in graph mode, around K launches of a
+graph of every layer's call, right after the timed steps, each after the
+lengths are restored (events cannot be recorded inside a captured graph on
+the runtime PyTorch ships). Also reported: per-step median and spread,
+repeated timed runs, the unfused path (Shared stage + Non-Shared stage +
+Merge) and the append alone, the Non-Shared stage's own HBM fraction, the
+box's streaming-read bandwidth, the PagedAttention-style comparison, and the
+fp64 oracle timed on the host's cores (a child process).
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
+import subprocess
 import sys
 import time
 
@@ -42,6 +52,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3       # fp32 vector
 
+DEFAULT_CONFIG = "5"
 DEFAULT_LAYERS = {"1": 16, "2": 16, "3": 6, "4A": 3, "4B": 2, "4B2g": 2, "4B2i": 2, "4B2d": 2, "5": 2}
 WORKLOAD_NAMES = {
     "1": "tiny fp32: R=1 P=256 B=4 L=2 4q/1kv D=64",
@@ -57,7 +68,7 @@ WORKLOAD_NAMES = {
 
 
 def _cfg_key(s):
-    return int(s) if s.isdigit() else s
+    return int(s) if str(s).isdigit() else s
 
 
 def algorithmic(w):
@@ -65,153 +76,17 @@ def algorithmic(w):
     e = w.elem_bytes
     # prompt rows once per distinct physical range (requests may alias one prefix)
     prompt_tokens = sum(p for (o, p) in {(int(w.prefix_off[r]), int(w.prefix_len[r])) for r in range(w.R)})
-    kv_tokens = prompt_tokens + int(sum(w.B * int(w.unshared_len[r]) for r in range(w.R)))
-    unique_kv = kv_tokens * w.Hkv * w.D * 2 * e
+    gen_tokens = int(sum(w.B * int(w.unshared_len[r]) for r in range(w.R)))
+    unique_kv = (prompt_tokens + gen_tokens) * w.Hkv * w.D * 2 * e
     q = w.N_b * w.Hq * w.D * e
     out = w.N_b * w.Hq * (w.D + 1) * 4
-    slots = int(sum(w.B * int(w.unshared_len[r]) for r in range(w.R))) * 4
+    slots = gen_tokens * 4
     total = unique_kv + q + out + slots
     mfma_flops = 4 * w.D * w.Hq * int(sum(w.B * int(w.prefix_len[r]) for r in range(w.R)))
     all_flops = 4 * w.D * w.Hq * int(sum(w.B * (int(w.prefix_len[r]) + int(w.unshared_len[r])) for r in range(w.R)))
-    return dict(unique_kv=unique_kv, total=total, mfma_flops=mfma_flops, flops=all_flops)
-
-
-def _oracle_state(w):
-    """Oracle cache state before the last step's append (untimed set-up)."""
-    import numpy as np
-    from oracle import append as oapp
-    kpool = np.zeros((max(w.num_slots, 1), w.Hkv, w.D), dtype=w.k_new.dtype)
-    vpool = np.zeros_like(kpool)
-    table = np.full((w.N_b, w.T_max), -1, dtype=np.int64)
-    ulen = np.zeros(w.R, dtype=np.int64)
-    for t in range(max(w.T_steps - 1, 0)):
-        oapp.cache_append(B=w.B, k_new=w.k_new[t], v_new=w.v_new[t], parent=w.parents[t],
-                          slot_base=w.slot_base, active=w.active(t), k_pool=kpool, v_pool=vpool,
-                          table_in=table, table_out=table, unshared_len=ulen)
-    return kpool, vpool, table, ulen
-
-
-def cpu_baseline(layers_np, min_seconds=10.0):
-    """Time the oracle (as it stands) on whole layer steps, the append of the
-    last step's tokens plus the decode attention, until min_seconds pass."""
-    from oracle import append as oapp
-    from oracle import pool
-    states = [_oracle_state(w) for w in layers_np]
-    done_beams = 0
-    done_layers = 0
-    workers = pool.host_cores()
-    used = workers
-    t0 = time.perf_counter()
-    i = 0
-    while True:
-        w = layers_np[i % len(layers_np)]
-        kpool, vpool, table, ulen = states[i % len(layers_np)]
-        if w.T_steps > 0:
-            t = w.T_steps - 1
-            u0 = ulen.copy()
-            tout = table.copy()
-            oapp.cache_append(B=w.B, k_new=w.k_new[t], v_new=w.v_new[t], parent=w.parents[t],
-                              slot_base=w.slot_base, active=w.active(t), k_pool=kpool, v_pool=vpool,
-                              table_in=table, table_out=tout, unshared_len=ulen)
-            ulen[:] = u0
-        _, _, dt, used = pool.attention_parallel(w, workers=workers)
-        done_beams += w.N_b
-        done_layers += 1
-        i += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    el = time.perf_counter() - t0
-    return dict(value=done_beams / el, unit="beams*layer-steps/s", cores=used, kind="oracle",
-                sample=f"{done_layers} full layer steps (append of the last step's tokens + decode) "
-                       f"of the same workload (fp64 numpy oracle, {used} worker processes, {el:.1f} s)")
-
-
-def paged_baseline(layers, K, xattn_decode_us, xattn_call_us, xattn_step_ms):
-    """The same layers in a PagedAttention-style block-paged cache: per layer,
-    the copies branching beams make of their partial tail blocks, then the
-    per-beam paged decode. HIP events around every call, K rounds, queued
-    behind each other (each call outlasts its host launch)."""
-    import numpy as np
-    import torch
-    from generative_recommendation_beam_amd import device as dv
-    from generative_recommendation_beam_amd import xattn
-    paged = []
-    for (d, o, lse, ws, nb, tin, tout, t_last) in layers:
-        pc = dv.build_paged(d, tout)
-        pnb = xattn.paged_workspace_size(d.dims, pc.max_seq_len)
-        pws = torch.zeros(max(pnb, 1), dtype=torch.uint8, device="cuda")
-        paged.append((d, pc, o, lse, pws, pnb))
-    torch.cuda.synchronize()
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    rounds = [[(ev(), ev(), ev()) for _ in paged] for _ in range(K)]
-    for d, pc, o, lse, pws, pnb in paged:  # warm-up
-        xattn.paged_copy_blocks(d.dims, pc.k_cache, pc.v_cache, pc.parent_tail, pc.spare)
-        dv.paged_decode(d, pc, o, lse, pws, pnb)
-    torch.cuda.synchronize()
-    start, end = ev(), ev()
-    start.record()
-    for r in rounds:
-        for (d, pc, o, lse, pws, pnb), (e0, e1, e2) in zip(paged, r):
-            e0.record()
-            xattn.paged_copy_blocks(d.dims, pc.k_cache, pc.v_cache, pc.parent_tail, pc.spare)
-            e1.record()
-            dv.paged_decode(d, pc, o, lse, pws, pnb)
-            e2.record()
-    end.record()
-    torch.cuda.synchronize()
-    copy_us = float(np.mean([[e0.elapsed_time(e1) for e0, e1, e2 in r] for r in rounds]) * 1e3)
-    dec_us = float(np.mean([[e1.elapsed_time(e2) for e0, e1, e2 in r] for r in rounds]) * 1e3)
-    step_ms = start.elapsed_time(end) / K
-    pc0 = paged[0][1]
-    return dict(decode_us_per_call=round(dec_us, 2), block_copy_us_per_call=round(copy_us, 2),
-                step_ms=round(step_ms, 4), blocks_per_layer=int(pc0.k_cache.shape[0]),
-                decode_speedup_xattn=round(dec_us / xattn_decode_us, 2),
-                layer_speedup_xattn=round((copy_us + dec_us) / xattn_call_us, 2),
-                step_speedup_xattn=round(step_ms / xattn_step_ms, 2),
-                note="same layers, same attention; PagedAttention-style per-beam paged decode "
-                     "(16-token blocks, prompt blocks shared and re-read by every beam) plus the "
-                     "copy each beam makes of its parent's tail block; eager launches. "
-                     "decode_speedup_xattn: against xattn's decode alone; layer_speedup_xattn: "
-                     "copy + decode against the fused append + decode call")
-
-
-def batch_former_timing():
-    """Host batch former (xattn_cht_*) on the Feather page's sensitivity
-    shape: 800 requests in 8 shuffled prefix groups, 1024-token prefixes plus
-    128 unique tokens, 16-token blocks; batches of up to 100 formed and
-    retired until none wait."""
-    import random
-    from generative_recommendation_beam_amd import xattn
-    rng = random.Random(11)
-    bs = 16
-    groups = [[rng.randint(0, 30000) for _ in range(1024)] for _ in range(8)]
-    order = [g for g in range(8) for _ in range(100)]
-    rng.shuffle(order)
-    reqs = [groups[g] + [rng.randint(0, 30000) for _ in range(128)] for g in order]
-    c = xattn.Cht(bs)
-    t0 = time.perf_counter()
-    for rid, toks in enumerate(reqs):
-        c.insert(rid, toks)
-    t1 = time.perf_counter()
-    batches, homogeneous = 0, 0
-    t_form = 0.0
-    while True:
-        s0 = time.perf_counter()
-        b = c.form_batch(100, 128 // bs)
-        t_form += time.perf_counter() - s0
-        if not b:
-            break
-        batches += 1
-        homogeneous += len({order[r] for r in b}) == 1
-        s0 = time.perf_counter()
-        for r in b:
-            c.complete(r)
-        t_form += time.perf_counter() - s0
-    c.close()
-    return dict(requests=len(reqs), insert_us_per_request=round((t1 - t0) / len(reqs) * 1e6, 2),
-                form_and_retire_us_per_request=round(t_form / len(reqs) * 1e6, 2), batches=batches,
-                homogeneous_batches=homogeneous,
-                note="host C++ through ctypes (the per-call Python overhead included)")
+    unshared = gen_tokens * w.Hkv * w.D * 2 * e + q + out + slots
+    return dict(unique_kv=unique_kv, total=total, mfma_flops=mfma_flops, flops=all_flops,
+                unshared_stage=unshared)
 
 
 def append_bytes(w):
@@ -255,199 +130,370 @@ def measured_traffic(cfg):
     return int(e["fetch_kib"] * 1024 * cal["fetch_factor"] + e["write_kib"] * 1024 * cal["write_factor"])
 
 
-def calibrate_copy(nbytes, reps):
-    """A plain device copy of known size, for scaling byte counters."""
-    import torch
-    torch.cuda.set_device(0)
-    n = nbytes // 4
-    src = torch.ones(n, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(reps):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "reps": reps}), flush=True)
+def _spread(xs):
+    xs = list(xs)
+    return dict(median=round(statistics.median(xs), 5), min=round(min(xs), 5), max=round(max(xs), 5),
+                stdev=round(statistics.pstdev(xs), 5), n=len(xs))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="2")
-    ap.add_argument("--layers", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--prefix-splits", type=int, default=0, help="override the split plan (0 = auto)")
-    ap.add_argument("--rows-per-block", type=int, default=0, help="override rows per workgroup (0 = auto)")
-    ap.add_argument("--stages", type=int, default=0, help="override LDS pipeline stages (0 = auto)")
-    ap.add_argument("--key-groups", type=int, default=0, help="override key groups per workgroup (0 = auto)")
-    ap.add_argument("--no-paged", action="store_true",
-                    help="skip the PagedAttention-style baseline measured beside the step")
-    ap.add_argument("--eager", action="store_true",
-                    help="launch every call from the host instead of one captured step graph")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
-                    help="only run a plain device copy of BYTES (counter calibration)")
-    args = ap.parse_args()
-    if args.calibrate_copy:
-        calibrate_copy(args.calibrate_copy, 3)
-        return
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(requests shard across GPUs with no exchange; see the design notes).",
-              file=sys.stderr)
-        sys.exit(2)
+class Setup:
+    """One workload's n_layers resident on the device, with its step graph."""
 
-    import numpy as np
-    import torch
+    def __init__(self, cfg, n_layers, args):
+        import torch
+        from generative_recommendation_beam_amd import device as dv
+        from generative_recommendation_beam_amd import inputs, xattn
+        self.cfg, self.n_layers, self.args = cfg, n_layers, args
+        self.layers_np = [inputs.config(cfg, layer=l) for l in range(n_layers)]
+        w0 = self.w0 = self.layers_np[0]
+        # One [n_layers][R] length array, restored with one copy per step.
+        self.ulen_all = torch.zeros((n_layers, max(w0.R, 1)), dtype=torch.int32, device="cuda")
+        self.layers = []
+        for l, w in enumerate(self.layers_np):
+            d = dv.upload(w, prefix_splits=args.prefix_splits, rows_per_block=args.rows_per_block,
+                          pipeline_stages=args.stages, key_groups=args.key_groups)
+            d.unshared_len = self.ulen_all[l]
+            table_in, table_out, t_last = dv.prepare_step(d)
+            o, lse, ws, nb = dv.alloc_outputs(d, 3 if t_last is not None else 2)
+            self.layers.append((d, o, lse, ws, nb, table_in, table_out, t_last))
+        self.ulen0 = self.ulen_all.clone()
+        # The step opens with the survivor selection (beam width x top-k pool
+        # per request, top-k = beam width) whose parents every layer's append reads.
+        self.topk_k = max(1, min(w0.B, 512))
+        tx = inputs.make_topk("select", R=w0.R, BW=w0.B, K=self.topk_k, n_out=w0.B, seed_key=(700, 0))
+        self.sel_in = [torch.from_numpy(v).cuda() for v in (tx.beam_score, tx.logprob, tx.token)]
+        self.sel_parent = torch.empty((w0.R, w0.B), dtype=torch.int32, device="cuda")
+        self.sel_tok = torch.empty_like(self.sel_parent)
+        self.sel_score = torch.empty((w0.R, w0.B), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        self.plan = xattn.get_plan(self.layers[0][0].dims, 2)
+        self.graphs = None
+        if not args.eager:
+            steps = []
+            for (d, o, lse, ws, nb, tin, tout, t_last) in self.layers:
+                st = dv.layer_step(d, o, lse, ws, nb, tin, tout, t_last)
+                st.parent = self.sel_parent.data_ptr()
+                steps.append(st)
+            sel = lambda: xattn.beam_select(*self.sel_in, w0.B, self.sel_parent, self.sel_tok, self.sel_score)
+            # the step; each layer's call alone, back to back (to time the
+            # dominant kernel with HIP events around its launches); the plain
+            # decodes on the complete caches; the selection alone
+            self.graphs = dict(
+                step=xattn.StepGraph(steps, select=sel()),
+                layer=xattn.StepGraph(steps),
+                decode=xattn.StepGraph([dv.layer_step(d, o, lse, ws, nb, None, tout, None)
+                                        for (d, o, lse, ws, nb, tin, tout, t_last) in self.layers]),
+                select=xattn.StepGraph([], select=sel()))
+            torch.cuda.synchronize()
 
-    from generative_recommendation_beam_amd import device as dv
-    from generative_recommendation_beam_amd import inputs, xattn
-
-    if not os.path.exists(xattn.LIB_PATH):
-        from generative_recommendation_beam_amd import build as _b
-        _b.build()
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
-    cfg = _cfg_key(args.config)
-    n_layers = args.layers or DEFAULT_LAYERS[str(cfg)]
-
-    layers_np = [inputs.config(cfg, layer=l) for l in range(n_layers)]
-    w0 = layers_np[0]
-    # One [n_layers][R] length array, restored with one copy per step.
-    ulen_all = torch.zeros((n_layers, max(w0.R, 1)), dtype=torch.int32, device="cuda")
-    layers = []
-    for l, w in enumerate(layers_np):
-        d = dv.upload(w, prefix_splits=args.prefix_splits, rows_per_block=args.rows_per_block,
-                      pipeline_stages=args.stages, key_groups=args.key_groups)
-        d.unshared_len = ulen_all[l]
-        table_in, table_out, t_last = dv.prepare_step(d)
-        o, lse, ws, nb = dv.alloc_outputs(d, 3 if t_last is not None else 2)
-        layers.append((d, o, lse, ws, nb, table_in, table_out, t_last))
-    ulen0 = ulen_all.clone()
-    # The step opens with the survivor selection (beam width x top-k pool per
-    # request, top-k = beam width) whose parents every layer's append reads.
-    topk_k = max(1, min(w0.B, 512))
-    tx = inputs.make_topk("select", R=w0.R, BW=w0.B, K=topk_k, n_out=w0.B, seed_key=(700, 0))
-    sel_in = [torch.from_numpy(v).cuda() for v in (tx.beam_score, tx.logprob, tx.token)]
-    sel_parent = torch.empty((w0.R, w0.B), dtype=torch.int32, device="cuda")
-    sel_tok = torch.empty_like(sel_parent)
-    sel_score = torch.empty((w0.R, w0.B), dtype=torch.float32, device="cuda")
-    torch.cuda.synchronize()
-    plan = xattn.get_plan(layers[0][0].dims, 2)
-    alg = algorithmic(w0)
-    K = args.steps
-
-    def new_events():
-        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in layers]
-
-    def eager_step(evs):
-        ulen_all.copy_(ulen0)
-        xattn.beam_topk(*sel_in, w0.B, sel_parent, sel_tok, sel_score)
-        for (d, o, lse, ws, nb, tin, tout, t_last), (e0, e1) in zip(layers, evs):
-            e0.record()
+    def eager_step(self, evs=None):
+        from generative_recommendation_beam_amd import xattn
+        self.ulen_all.copy_(self.ulen0)
+        xattn.beam_topk(*self.sel_in, self.w0.B, self.sel_parent, self.sel_tok, self.sel_score)
+        for i, (d, o, lse, ws, nb, tin, tout, t_last) in enumerate(self.layers):
+            if evs is not None:
+                evs[i][0].record()
             if t_last is not None:
                 xattn.append_decode(d.dims, q=d.q, k_shared=d.k_shared, v_shared=d.v_shared,
                                     prefix_off=d.prefix_off, prefix_len=d.prefix_len, k_new=d.k_new[t_last],
-                                    v_new=d.v_new[t_last], parent=sel_parent, slot_base=d.slot_base,
+                                    v_new=d.v_new[t_last], parent=self.sel_parent, slot_base=d.slot_base,
                                     active=d.active[t_last], k_pool=d.k_pool, v_pool=d.v_pool, table_in=tin,
                                     table_out=tout, unshared_len=d.unshared_len, o=o, lse=lse,
                                     workspace=ws if nb else None, workspace_bytes=nb)
             else:
                 xattn.decode(d.dims, d.q, d.k_shared, d.v_shared, d.prefix_off, d.prefix_len, d.k_pool,
                              d.v_pool, tout, d.unshared_len, o, lse, ws if nb else None, nb)
-            e1.record()
+            if evs is not None:
+                evs[i][1].record()
 
-    step_evs = [new_events() for _ in range(K)] if args.eager else []
-    warm_evs = new_events()
-    if not args.eager:
-        # The whole step (every layer's append and decode) as one graph.
-        steps = []
-        for (d, o, lse, ws, nb, tin, tout, t_last) in layers:
-            st = dv.layer_step(d, o, lse, ws, nb, tin, tout, t_last)
-            st.parent = sel_parent.data_ptr()
-            steps.append(st)
-        select = xattn.beam_select(*sel_in, w0.B, sel_parent, sel_tok, sel_score)
-        step_graph = xattn.StepGraph(steps, select=select)
-        select_graph = xattn.StepGraph([], select=xattn.beam_select(*sel_in, w0.B, sel_parent, sel_tok,
-                                                                    sel_score))
-        # Every layer's call alone, back to back in one graph, to time the
-        # dominant kernel with HIP events around its launches (the runtime
-        # PyTorch ships cannot record events inside a captured graph); and
-        # the plain decodes on the complete caches, for reference.
-        layer_graph = xattn.StepGraph(steps)
-        decode_graph = xattn.StepGraph([dv.layer_step(d, o, lse, ws, nb, None, tout, None)
-                                        for (d, o, lse, ws, nb, tin, tout, t_last) in layers])
-        torch.cuda.synchronize()
-
-    def one_step(k):
-        if args.eager:
-            eager_step(warm_evs if k < 0 else step_evs[k])
+    def one_step(self, evs=None):
+        if self.graphs is None:
+            self.eager_step(evs)
         else:
-            ulen_all.copy_(ulen0)
-            step_graph.launch()
+            self.ulen_all.copy_(self.ulen0)
+            self.graphs["step"].launch()
 
-    for _ in range(args.warmup):
-        one_step(-1)
+    def close(self):
+        if self.graphs:
+            for g in self.graphs.values():
+                g.close()
+        self.graphs = None
+
+
+def _ev():
+    import torch
+    return torch.cuda.Event(enable_timing=True)
+
+
+def time_steps(s, K, warmup, repeats):
+    """K timed steps after `warmup` untimed ones, bracketed by synchronizes;
+    per-step events give the median and spread; `repeats` more timed runs of
+    K steps give the run-to-run spread."""
+    import torch
+    for _ in range(warmup):
+        s.one_step()
     torch.cuda.synchronize()
-
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    per_step = [(_ev(), _ev()) for _ in range(K)]
+    call_evs = [[(_ev(), _ev()) for _ in s.layers] for _ in range(K)] if s.graphs is None else None
+    start, end = _ev(), _ev()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for k in range(K):
-        one_step(k)
+        per_step[k][0].record()
+        s.one_step(None if call_evs is None else call_evs[k])
+        per_step[k][1].record()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
-    select_us = None
-    decode_only_us = None
-    if args.eager:
-        call_ms = np.array([[e0.elapsed_time(e1) for (e0, e1) in evs] for evs in step_evs])
-        call_us = float(call_ms.mean() * 1e3)
-    else:
-        # Kernel timing pass, right after the timed steps, on the state they
-        # leave (every layer's cache complete): K launches of the graph of
-        # every layer's decode, each between two HIP events on the launch
-        # stream; a decode's duration is the pair's interval / n_layers
-        # (back-to-back kernels of one graph: only graph-internal gaps added).
-        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(K)]
-        for e0, e1 in pairs:
-            ulen_all.copy_(ulen0)  # the same append every launch
-            e0.record()
-            layer_graph.launch()
-            e1.record()
-        dpairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(K)]
-        for e0, e1 in dpairs:
-            e0.record()
-            decode_graph.launch()
-            e1.record()
-        spairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(K)]
-        for e0, e1 in spairs:
-            e0.record()
-            select_graph.launch()
-            e1.record()
+    step_ms = [a.elapsed_time(b) for a, b in per_step]
+    reps = []
+    for _ in range(repeats):
+        a, b = _ev(), _ev()
         torch.cuda.synchronize()
-        call_us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in pairs]) * 1e3 / n_layers)
-        decode_only_us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in dpairs]) * 1e3 / n_layers)
-        select_us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in spairs]) * 1e3)
-        step_graph.close()
-        layer_graph.close()
-        decode_graph.close()
-        select_graph.close()
+        a.record()
+        for k in range(K):
+            s.one_step()
+        b.record()
+        torch.cuda.synchronize()
+        reps.append(a.elapsed_time(b) / K)
+    call_us = None
+    if call_evs is not None:
+        call_us = [a.elapsed_time(b) * 1e3 for evs in call_evs for a, b in evs]
+    return dict(ms_total=ms_total, wall=wall, step_ms=step_ms, repeat_ms_per_step=reps, eager_call_us=call_us)
 
-    ms_per_step = ms_total / K
+
+def time_graph(g, K, before=None):
+    """Mean and per-launch ms of K launches of graph g, each between two HIP
+    events on the launch stream (`before` runs outside the events)."""
+    import torch
+    pairs = [(_ev(), _ev()) for _ in range(K)]
+    for e0, e1 in pairs:
+        if before is not None:
+            before()
+        e0.record()
+        g.launch()
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in pairs]
+
+
+def time_parts(s, K):
+    """The same layers through the separate calls, eager, HIP events around
+    each: the unfused path (Shared stage, Non-Shared stage, Merge) on the
+    complete caches, and the append alone (lengths restored before each
+    round, outside the events)."""
+    import numpy as np
+    import torch
+    from generative_recommendation_beam_amd import xattn
+    bufs = []
+    for (d, o, lse, ws, nb, tin, tout, t_last) in s.layers:
+        rows, D = d.rows, d.w.D
+        n0 = xattn.workspace_size(d.dims, 0)
+        n1 = xattn.workspace_size(d.dims, 1)
+        bufs.append(dict(os=torch.empty((rows, D), dtype=torch.float32, device="cuda"),
+                         ls=torch.empty(rows, dtype=torch.float32, device="cuda"),
+                         ou=torch.empty((rows, D), dtype=torch.float32, device="cuda"),
+                         lu=torch.empty(rows, dtype=torch.float32, device="cuda"),
+                         w0=torch.zeros(max(n0, 1), dtype=torch.uint8, device="cuda"), n0=n0,
+                         w1=torch.zeros(max(n1, 1), dtype=torch.uint8, device="cuda"), n1=n1,
+                         tscratch=torch.empty_like(tout)))
+
+    def unfused(evs):
+        for (d, o, lse, ws, nb, tin, tout, t_last), b, e in zip(s.layers, bufs, evs):
+            e[0].record()
+            xattn.shared_stage(d.dims, d.q, d.k_shared, d.v_shared, d.prefix_off, d.prefix_len, b["os"], b["ls"],
+                               b["w0"] if b["n0"] else None, b["n0"])
+            e[1].record()
+            xattn.unshared_stage(d.dims, d.q, d.k_pool, d.v_pool, tout, d.unshared_len, b["ou"], b["lu"],
+                                 b["w1"] if b["n1"] else None, b["n1"])
+            e[2].record()
+            xattn.merge(d.rows, d.w.D, b["os"], b["ls"], b["ou"], b["lu"], o, lse)
+            e[3].record()
+
+    def appends(evs):
+        s.ulen_all.copy_(s.ulen0)
+        for (d, o, lse, ws, nb, tin, tout, t_last), b, e in zip(s.layers, bufs, evs):
+            e[0].record()
+            xattn.cache_append(d.dims, d.k_new[t_last], d.v_new[t_last], s.sel_parent, d.slot_base,
+                               d.active[t_last], d.k_pool, d.v_pool, tin, b["tscratch"], d.unshared_len)
+            e[1].record()
+
+    # complete caches: lengths as after the step
+    s.one_step()
+    torch.cuda.synchronize()
+    unfused([[_ev() for _ in range(4)] for _ in s.layers])  # warm-up
+    rounds = [[[_ev() for _ in range(4)] for _ in s.layers] for _ in range(K)]
+    for r in rounds:
+        unfused(r)
+    torch.cuda.synchronize()
+    sh = np.array([[e[0].elapsed_time(e[1]) for e in r] for r in rounds]) * 1e3
+    un = np.array([[e[1].elapsed_time(e[2]) for e in r] for r in rounds]) * 1e3
+    mg = np.array([[e[2].elapsed_time(e[3]) for e in r] for r in rounds]) * 1e3
+    out = dict(shared_us=round(float(np.median(sh)), 3), unshared_us=round(float(np.median(un)), 3),
+               merge_us=round(float(np.median(mg)), 3))
+    out["unfused_us"] = round(out["shared_us"] + out["unshared_us"] + out["merge_us"], 3)
+    if s.layers[0][7] is not None:
+        appends([[_ev(), _ev()] for _ in s.layers])
+        ar = [[[_ev(), _ev()] for _ in s.layers] for _ in range(K)]
+        for r in ar:
+            appends(r)
+        torch.cuda.synchronize()
+        out["append_us"] = round(float(np.median([[e[0].elapsed_time(e[1]) for e in r] for r in ar])) * 1e3, 3)
+    # leave the caches as a step leaves them
+    s.one_step()
+    torch.cuda.synchronize()
+    return out
+
+
+def stream_bandwidth(nbytes=4 << 30, reps=10):
+    """GB/s of the library's streaming-read kernel over nbytes of HBM."""
+    import torch
+    from generative_recommendation_beam_amd import xattn
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        xattn.stream_read(buf, sink)
+    ms = []
+    for _ in range(reps):
+        a, b = _ev(), _ev()
+        a.record()
+        xattn.stream_read(buf, sink)
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    del buf
+    med = statistics.median(ms)
+    return dict(read_GBps=round(nbytes / (med * 1e-3) / 1e9, 1), bytes=nbytes, reps=reps,
+                frac_of_peak=round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                kernel="xattn_stream_read (16-byte loads, data discarded), median of the launches")
+
+
+def cpu_baseline(cfg, seconds, single_core, single_seconds):
+    """The fp64 oracle as it stands, timed on this host's cores in a child
+    process (BLAS pinned to one thread per process before numpy loads)."""
+    cmd = [sys.executable, "-m", "oracle.timing", "--config", str(cfg), "--seconds", str(seconds),
+           "--single-core", ",".join(single_core), "--single-seconds", str(single_seconds)]
+    r = subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True, timeout=1200)
+    if r.returncode != 0:
+        raise RuntimeError(f"oracle timing failed ({r.returncode}):\n{r.stderr[-2000:]}")
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def paged_baseline(s, K, xattn_decode_us, xattn_call_us, xattn_step_ms):
+    """The same layers in a PagedAttention-style block-paged cache: per layer,
+    the copies branching beams make of their partial tail blocks, then the
+    per-beam paged decode. HIP events around every call, K rounds, queued
+    behind each other (each call outlasts its host launch)."""
+    import numpy as np
+    import torch
+    from generative_recommendation_beam_amd import device as dv
+    from generative_recommendation_beam_amd import xattn
+    paged = []
+    for (d, o, lse, ws, nb, tin, tout, t_last) in s.layers:
+        pc = dv.build_paged(d, tout)
+        pnb = xattn.paged_workspace_size(d.dims, pc.max_seq_len)
+        pws = torch.zeros(max(pnb, 1), dtype=torch.uint8, device="cuda")
+        paged.append((d, pc, o, lse, pws, pnb))
+    torch.cuda.synchronize()
+    rounds = [[(_ev(), _ev(), _ev()) for _ in paged] for _ in range(K)]
+    for d, pc, o, lse, pws, pnb in paged:  # warm-up
+        xattn.paged_copy_blocks(d.dims, pc.k_cache, pc.v_cache, pc.parent_tail, pc.spare)
+        dv.paged_decode(d, pc, o, lse, pws, pnb)
+    torch.cuda.synchronize()
+    start, end = _ev(), _ev()
+    start.record()
+    for r in rounds:
+        for (d, pc, o, lse, pws, pnb), (e0, e1, e2) in zip(paged, r):
+            e0.record()
+            xattn.paged_copy_blocks(d.dims, pc.k_cache, pc.v_cache, pc.parent_tail, pc.spare)
+            e1.record()
+            dv.paged_decode(d, pc, o, lse, pws, pnb)
+            e2.record()
+    end.record()
+    torch.cuda.synchronize()
+    copy_us = float(np.mean([[e0.elapsed_time(e1) for e0, e1, e2 in r] for r in rounds]) * 1e3)
+    dec_us = float(np.mean([[e1.elapsed_time(e2) for e0, e1, e2 in r] for r in rounds]) * 1e3)
+    step_ms = start.elapsed_time(end) / K  # every layer's copies and decode
+    pc0 = paged[0][1]
+    del paged
+    torch.cuda.empty_cache()
+    return dict(decode_us_per_call=round(dec_us, 2), block_copy_us_per_call=round(copy_us, 2),
+                step_ms=round(step_ms, 4), blocks_per_layer=int(pc0.k_cache.shape[0]), rounds=K,
+                decode_speedup_xattn=round(dec_us / xattn_decode_us, 2),
+                layer_speedup_xattn=round((copy_us + dec_us) / xattn_call_us, 2),
+                step_speedup_xattn=round(step_ms / xattn_step_ms, 2),
+                note="same layers, same attention; PagedAttention-style per-beam paged decode "
+                     "(16-token blocks, prompt blocks shared and re-read by every beam) plus the "
+                     "copy each beam makes of its parent's tail block; eager launches. "
+                     "decode_speedup_xattn: against xattn's decode alone; layer_speedup_xattn: "
+                     "copy + decode against the fused append + decode call; step_ms: every "
+                     "layer's copies and decode, against xattn's whole step")
+
+
+def batch_former_timing():
+    """Host batch former (xattn_cht_*) on the Feather page's sensitivity
+    shape: 800 requests in 8 shuffled prefix groups, 1024-token prefixes plus
+    128 unique tokens, 16-token blocks; batches of up to 100 formed and
+    retired until none wait."""
+    import random
+    from generative_recommendation_beam_amd import xattn
+    rng = random.Random(11)
+    bs = 16
+    groups = [[rng.randint(0, 30000) for _ in range(1024)] for _ in range(8)]
+    order = [g for g in range(8) for _ in range(100)]
+    rng.shuffle(order)
+    reqs = [groups[g] + [rng.randint(0, 30000) for _ in range(128)] for g in order]
+    c = xattn.Cht(bs)
+    t0 = time.perf_counter()
+    for rid, toks in enumerate(reqs):
+        c.insert(rid, toks)
+    t1 = time.perf_counter()
+    batches, homogeneous = 0, 0
+    t_form = 0.0
+    while True:
+        s0 = time.perf_counter()
+        b = c.form_batch(100, 128 // bs)
+        t_form += time.perf_counter() - s0
+        if not b:
+            break
+        batches += 1
+        homogeneous += len({order[r] for r in b}) == 1
+        s0 = time.perf_counter()
+        for r in b:
+            c.complete(r)
+        t_form += time.perf_counter() - s0
+    c.close()
+    return dict(requests=len(reqs), insert_us_per_request=round((t1 - t0) / len(reqs) * 1e6, 2),
+                form_and_retire_us_per_request=round(t_form / len(reqs) * 1e6, 2), batches=batches,
+                homogeneous_batches=homogeneous,
+                note="host C++ through ctypes (the per-call Python overhead included)")
+
+
+def measure(cfg, args, *, paged_rounds):
+    """Every GPU figure of one workload: the timed steps (value), the
+    dominant kernel's roofline, the separate calls and the comparison."""
+    import numpy as np
+    import torch
+    n_layers = args.layers or DEFAULT_LAYERS[str(cfg)]
+    s = Setup(cfg, n_layers, args)
+    w0, K = s.w0, args.steps
+    print(f"[{cfg}] timing {K} steps of {n_layers} layers ...", file=sys.stderr, flush=True)
+    st = time_steps(s, K, args.warmup, args.repeats)
+    ms_per_step = st["ms_total"] / K
     value = w0.N_b * n_layers / (ms_per_step / 1e3)
-    # The timed call is the fused append + decode when the layers append
-    # (one launch when the plan folds the append in): its bytes include the
-    # append's.
-    appends = layers[0][7] is not None
-    fused = appends and plan["mfma"] == 1 and plan["partials"] == 0
+    restore = lambda: s.ulen_all.copy_(s.ulen0)  # the same append every launch
+    if s.graphs is None:
+        call_us = float(np.mean(st["eager_call_us"]))
+        decode_only_us = select_us = None
+    else:
+        call_us = float(np.mean(time_graph(s.graphs["layer"], K, restore))) * 1e3 / n_layers
+        decode_only_us = float(np.mean(time_graph(s.graphs["decode"], K))) * 1e3 / n_layers
+        select_us = float(np.mean(time_graph(s.graphs["select"], K))) * 1e3
+    alg = algorithmic(w0)
+    appends = s.layers[0][7] is not None
+    fused = appends and s.plan["mfma"] == 1 and s.plan["partials"] == 0
     call_bytes = alg["total"] + (append_bytes(w0) if appends else 0)
     t_hbm = call_bytes / (PEAK_HBM_GBS * 1e9)
     peak_tflops = PEAK_BF16_TFLOPS if w0.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -465,53 +511,130 @@ def main():
         roof["kernel"] = "xattn_append_decode call (1 kernel launch: the append folded into the decode)"
     elif appends:
         roof["kernel"] = "xattn_append_decode call (append, then %d decode launch%s)" % (
-            plan["launches"], "" if plan["launches"] == 1 else "es")
+            s.plan["launches"], "" if s.plan["launches"] == 1 else "es")
     else:
-        roof["kernel"] = "xattn_decode call (%d kernel launch%s)" % (plan["launches"], "" if plan["launches"] == 1 else "es")
+        roof["kernel"] = "xattn_decode call (%d kernel launch%s)" % (
+            s.plan["launches"], "" if s.plan["launches"] == 1 else "es")
     roof["timing"] = ("HIP events around K launches of a graph of the n_layers calls (interval / "
                       "n_layers; lengths restored before each launch, outside the events), run right "
-                      "after the timed steps" if not args.eager else
+                      "after the timed steps" if s.graphs is not None else
                       "HIP events around every call of the timed steps")
     roof["avg_call_us"] = round(call_us, 3)
     if decode_only_us is not None:
         roof["decode_only_us"] = round(decode_only_us, 3)
     roof["algorithmic_bytes_per_call"] = call_bytes
     roof["algorithmic_mfma_flops_per_call"] = alg["mfma_flops"]
+    roof["hbm_frac_algorithmic"] = round(call_bytes / call_s / 1e9 / PEAK_HBM_GBS, 4)
+    roof["mfma_frac_algorithmic"] = round(alg["mfma_flops"] / call_s / 1e12 / peak_tflops, 4)
     roof["kernel_hash"] = kernel_hash()
-
-    result = {
-        "metric": "beam-decode attention beams*layer-steps/s; achieved HBM GB/s vs peak",
+    print(f"[{cfg}] timing the separate calls ...", file=sys.stderr, flush=True)
+    parts = time_parts(s, min(K, 20))
+    ns_s = parts["unshared_us"] * 1e-6
+    parts["nonshared_stage"] = dict(
+        us=parts["unshared_us"], algorithmic_bytes=alg["unshared_stage"],
+        achieved_GBps=round(alg["unshared_stage"] / ns_s / 1e9, 1),
+        frac_of_hbm_peak=round(alg["unshared_stage"] / ns_s / 1e9 / PEAK_HBM_GBS, 4),
+        bytes="generated K/V once per beam + Q + O + lse + slot indices")
+    parts["unfused_vs_fused"] = round(parts["unfused_us"] / (decode_only_us or call_us), 3)
+    res = {
         "value": round(value, 1),
-        "unit": "beams*layer-steps/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w0.dtype,
-        "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[str(cfg)], "n_layers": n_layers,
-                   "beams_per_call": w0.N_b,
+        "step_ms_spread": _spread(st["step_ms"]),
+        "repeat_ms_per_step": [round(x, 5) for x in st["repeat_ms_per_step"]],
+        "wall_s_timed": round(st["wall"], 4),
+        "config": {"workload": WORKLOAD_NAMES[str(cfg)], "n_layers": n_layers, "beams_per_call": w0.N_b,
                    "step": "beam selection (%d x %d x %d pool -> %d beams per request), then "
-                           "append + decode per layer (one xattn_append_decode call)" % (w0.R, w0.B, topk_k, w0.B),
-                   "launch": "eager" if args.eager else "graph", "plan": plan},
+                           "append + decode per layer (one xattn_append_decode call)" % (
+                               w0.R, w0.B, s.topk_k, w0.B),
+                   "launch": "eager" if s.graphs is None else "graph", "plan": s.plan},
+        "dtype": w0.dtype,
         "unique_kv_GBps": round(alg["unique_kv"] / call_s / 1e9, 1),
         "total_GBps": round(call_bytes / call_s / 1e9, 1),
         "mfma_TFLOPs": round(alg["mfma_flops"] / call_s / 1e12, 1),
-        "wall_s_timed": round(wall, 4),
-        "step_GBps": round(n_layers * (alg["total"] + append_bytes(w0)) / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_GBps": round(n_layers * call_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "roofline": roof,
         "beam_select_us": None if select_us is None else round(select_us, 3),
+        "separate_calls": parts,
     }
-    if not args.no_paged and w0.dtype == "bf16":
-        print("timing the PagedAttention-style baseline ...", file=sys.stderr, flush=True)
-        result["paged_baseline"] = paged_baseline(layers, K, decode_only_us or call_us, call_us, ms_per_step)
+    if paged_rounds and w0.dtype == "bf16":
+        print(f"[{cfg}] timing the PagedAttention-style baseline ...", file=sys.stderr, flush=True)
+        res["paged_baseline"] = paged_baseline(s, paged_rounds, decode_only_us or call_us, call_us, ms_per_step)
+    s.close()
+    del s
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--repeats", type=int, default=2, help="extra timed runs of K steps (run-to-run spread)")
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--extra-configs", default=None,
+                    help="comma list measured after the headline (default: 2 with the default headline)")
+    ap.add_argument("--layers", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--prefix-splits", type=int, default=0, help="override the split plan (0 = auto)")
+    ap.add_argument("--rows-per-block", type=int, default=0, help="override rows per workgroup (0 = auto)")
+    ap.add_argument("--stages", type=int, default=0, help="override LDS pipeline stages (0 = auto)")
+    ap.add_argument("--key-groups", type=int, default=0, help="override key groups per workgroup (0 = auto)")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the PagedAttention-style baseline measured beside the step")
+    ap.add_argument("--no-stream", action="store_true", help="skip the streaming-read bandwidth")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every call from the host instead of one captured step graph")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requests shard across GPUs with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from generative_recommendation_beam_amd import xattn
+
+    if not os.path.exists(xattn.LIB_PATH):
+        raise SystemExit(f"bench.py: {xattn.LIB_PATH} is not built (run __graft_entry__.build())")
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = _cfg_key(args.config)
+    extras = args.extra_configs
+    if extras is None:
+        extras = "2" if str(cfg) == DEFAULT_CONFIG else ""
+    extras = [_cfg_key(c) for c in extras.split(",") if c]
+
+    head = measure(cfg, args, paged_rounds=0 if args.no_paged else min(args.steps, 5))
+    result = {
+        "metric": "beam-decode attention beams*layer-steps/s; achieved HBM GB/s vs peak",
+        "value": head.pop("value"),
+        "unit": "beams*layer-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head.pop("dtype"),
+        "data": "synthetic",
+        "config": head.pop("config"),
+    }
+    result.update(head)
+    for c in extras:
+        ex = measure(c, args, paged_rounds=0 if args.no_paged else min(args.steps, 20))
+        result[f"config_{c}"] = ex
+    if not args.no_stream:
+        result["hbm_stream_read"] = stream_bandwidth()
     result["batch_former"] = batch_former_timing()
     if not args.no_cpu_baseline:
-        print("timing the oracle on host cores ...", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(layers_np, args.cpu_seconds)
+        print("timing the oracle on host cores (child process) ...", file=sys.stderr, flush=True)
+        cb = cpu_baseline(cfg, args.cpu_seconds, ["1", "2", "4A"], 5.0)
+        result["cpu_baseline"] = cb["multi"]
+        result["cpu_baseline_single_core"] = cb["single_core"]
     print(json.dumps(result), flush=True)
 
 

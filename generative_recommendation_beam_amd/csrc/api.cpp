@@ -76,7 +76,12 @@ xattn_status check_dims(const xattn_dims* d) {
     return XATTN_ERR_INVALID_ARG;
   if (d->key_groups < 0 || d->key_groups == 3 || d->key_groups > 4) return XATTN_ERR_INVALID_ARG;
   if (d->key_groups == 4 && d->pipeline_stages == 4) return XATTN_ERR_INVALID_ARG;  // LDS
-  if (!(d->scale == d->scale)) return XATTN_ERR_INVALID_ARG;  // NaN
+  // The scale must be finite and positive: the kernels take a tile's running
+  // maximum as max(q.k) * scale (a negative scale would make it the minimum)
+  // and multiply masked scores of -inf by it (0 or inf would give NaN).
+  // The kernels fold log2(e) into it, so that product must stay finite too.
+  const float scale_log2 = d->scale * 1.4426950408889634f;
+  if (!(d->scale > 0.0f && scale_log2 <= 3.4028234663852886e38f)) return XATTN_ERR_INVALID_ARG;
   if (d->head_dim != 64 && d->head_dim != 128) return XATTN_ERR_UNSUPPORTED;
   if (d->key_groups == 4 && d->head_dim != 128) return XATTN_ERR_UNSUPPORTED;
   if (d->key_groups == 4 && d->rows_per_block == 128) return XATTN_ERR_UNSUPPORTED;  // 16 waves
@@ -671,6 +676,12 @@ xattn_status xattn_paged_copy_blocks(const xattn_dims* d, void* k_cache, void* v
   const int64_t block_elems = (int64_t)d->num_kv_heads * kPagedBlock * d->head_dim;
   return hip_status(launch_copy_blocks(static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), src,
                                        dst, n, block_elems, static_cast<hipStream_t>(stream)));
+}
+
+xattn_status xattn_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0) return XATTN_OK;
+  if (!src || !sink || !aligned16(src) || bytes % 16 != 0) return XATTN_ERR_INVALID_ARG;
+  return hip_status(launch_stream_read(src, (int64_t)bytes, sink, static_cast<hipStream_t>(stream)));
 }
 
 xattn_status xattn_beam_topk(int32_t num_requests, int32_t beam_width, int32_t top_k, int32_t n_out,

@@ -165,4 +165,7 @@ hipError_t launch_paged_attn(const PagedArgs& a, hipStream_t st);
 hipError_t launch_copy_blocks(uint16_t* kc, uint16_t* vc, const int32_t* src, const int32_t* dst, int n,
                               int64_t block_elems, hipStream_t st);
 
+// ---- Streaming-read measurement (stream.hip) ----
+hipError_t launch_stream_read(const void* src, int64_t bytes, unsigned* sink, hipStream_t st);
+
 }  // namespace xattn

@@ -135,9 +135,10 @@ __device__ __forceinline__ void wait_vmem() { __asm__ volatile("s_waitcnt vmcnt(
 
 // Split partials that one workgroup hands to another are written and read
 // with agent-coherent buffer accesses (cache policy sc1, what agent-scope
-// atomic loads/stores use), so no cache-wide flush or invalidate is needed:
-// writers wait for their stores to complete, then bump a relaxed agent-scope
-// counter; the last arrival reads the partials back with the same policy.
+// atomic loads/stores use). The hand-over itself follows the agent-scope
+// release/acquire pattern: writers wait for their stores, fence (release,
+// agent) and arrive on a counter with an acquire-release atomic; the last
+// arrival fences (acquire, agent) before it reads the partials back.
 constexpr int kCoherent = 16;  // sc1
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -1036,15 +1037,22 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
                                               kCoherent);
     }
   }
+  // Publish: every thread's partial stores are released at agent scope (the
+  // members of a group may run on different XCDs, each with its own L2)
+  // before the workgroup barrier, and the arrival is an acquire-release
+  // agent-scope atomic; the last arrival acquires at agent scope before it
+  // reads the partials back.
   wait_vmem();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (tid == 0) {
     const unsigned old = __builtin_amdgcn_atomic_inc32(a.counters + (int64_t)pair * a.row_tiles + tile,
-                                                       (unsigned)(members - 1), __ATOMIC_RELAXED, "agent");
+                                                       (unsigned)(members - 1), __ATOMIC_ACQ_REL, "agent");
     s_last = (old == (unsigned)(members - 1)) ? 1 : 0;
   }
   __syncthreads();
   if (!s_last || !row_ok) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   // Last arrival: combine every member's partial, always in member order, so
   // the result does not depend on which workgroup arrived last. Pass 1 finds
   // the largest lse; pass 2 sums the weighted outputs (independent loads).

@@ -5,8 +5,8 @@ them out in the device layouts the C-ABI documents. It holds none of the
 attention arithmetic and imports neither the HIP binding nor the oracle; both
 sides consume the arrays it returns.
 
-Workload shapes follow the xGR page ("xGR: Efficient Generative Recommendation
-Serving at Scale"): long user-history prompts with short fixed-length outputs
+Workload shapes follow the xGR page ("xGR: Atendimento de Recomendação Generativa
+Eficiente em Escala"): long user-history prompts with short fixed-length outputs
 (section 1, workload mismatch bullet), beam widths from 128 to 512 (section 1,
 beam-search overhead bullet; section 4, scalability bullet), and prompts of a
 few thousand tokens (section 4, memory bullet). The prefix-homogeneous batch
@@ -45,9 +45,11 @@ def _rng(seed_key, tag: int) -> np.random.Generator:
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit pattern, round to nearest even (finite inputs)."""
-    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    lsb = (bits >> np.uint64(16)) & np.uint64(1)
-    return ((bits + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+    # 32-bit arithmetic suffices: for finite inputs the largest pattern,
+    # 0xFF7FFFFF, plus the rounding bias stays below 2^32.
+    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (bits >> np.uint32(16)) & np.uint32(1)
+    return ((bits + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:

@@ -24,7 +24,8 @@ EXPORTED = ("xattn_workspace_size", "xattn_get_plan", "xattn_shared_stage", "xat
             "xattn_paged_workspace_size", "xattn_paged_decode", "xattn_paged_copy_blocks",
             "xattn_cht_create", "xattn_cht_destroy", "xattn_cht_insert", "xattn_cht_best",
             "xattn_cht_admit", "xattn_cht_complete", "xattn_cht_form_batch", "xattn_step_graph_create",
-            "xattn_step_graph_launch", "xattn_step_graph_destroy", "xattn_status_string")
+            "xattn_step_graph_launch", "xattn_step_graph_destroy", "xattn_stream_read",
+            "xattn_status_string")
 
 
 class Dims(ctypes.Structure):
@@ -142,6 +143,8 @@ def lib():
     L.xattn_step_graph_launch.argtypes = [P, P]
     L.xattn_step_graph_destroy.restype = ctypes.c_int
     L.xattn_step_graph_destroy.argtypes = [P]
+    L.xattn_stream_read.restype = ctypes.c_int
+    L.xattn_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
     _lib = L
     return L
 
@@ -243,6 +246,12 @@ def append_decode(dims, q, k_shared, v_shared, prefix_off, prefix_len, k_new, v_
                                      _ptr(o), _ptr(lse), _ptr(workspace), int(workspace_bytes),
                                      _stream(stream)),
            "xattn_append_decode")
+
+
+def stream_read(src, sink, nbytes=None, stream=None):
+    """Measurement utility: read `nbytes` (default: all) of tensor src once."""
+    nbytes = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    _check(lib().xattn_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "xattn_stream_read")
 
 
 def paged_workspace_size(dims, max_seq_len) -> int:

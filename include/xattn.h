@@ -2,8 +2,8 @@
  * xattn.h - staged beam-search decode attention over a split KV cache,
  * hand-written HIP kernels for AMD Instinct MI355X (gfx950, CDNA4).
  *
- * The method (xGR page, "xGR: Efficient Generative Recommendation Serving at
- * Scale", section 2.1 xAttention): the KV cache of a generative-recommendation
+ * The method (xGR page, "xGR: Atendimento de Recomendação Generativa Eficiente
+ * em Escala", section 2.1 xAttention): the KV cache of a generative-recommendation
  * request is split in two. The Shared cache holds the prompt (user history),
  * computed once at prefill and read once for all beams of the request. The
  * Non-Shared cache holds only the tokens generated at each decode step,
@@ -83,7 +83,8 @@ typedef struct {
   int32_t dtype;            /* xattn_dtype of q and every K/V buffer */
   int64_t num_slots;        /* capacity of k_pool / v_pool in tokens */
   int64_t num_prefix_tokens;/* n_ptok: token extent of k_shared / v_shared */
-  float scale;              /* softmax scale applied to q.k (normally 1/sqrt(D)) */
+  float scale;              /* softmax scale applied to q.k (normally 1/sqrt(D)); must be
+                               finite and > 0, else XATTN_ERR_INVALID_ARG */
   int32_t prefix_splits;    /* 0 = automatic; else force this many prefix splits */
   int32_t unshared_splits;  /* 0 = automatic; else force this many Non-Shared splits
                                (forces the Non-Shared part out of the fused epilogue) */
@@ -417,6 +418,20 @@ xattn_status xattn_cht_admit(xattn_cht* cht, int64_t request_id);
 xattn_status xattn_cht_complete(xattn_cht* cht, int64_t request_id);
 xattn_status xattn_cht_form_batch(xattn_cht* cht, int32_t max_batch, int64_t max_missing,
                                   int64_t* out_ids, int32_t* out_n);
+
+/*
+ * MEASUREMENT UTILITY (not part of the attention path): reads `bytes` of
+ * device memory at src once, with 16-byte vector loads spread over every CU,
+ * and discards the data. Timing it gives the practical HBM read ceiling that
+ * the attention kernels' bandwidth figures are read against (xGR page,
+ * section 4: the baseline kernel's memory pipeline is reported busy most of
+ * the time, so the attainable bandwidth is the yardstick; the 8 TB/s of the
+ * data sheet is not reachable by any kernel). src must be 16-byte aligned
+ * and bytes a multiple of 16 (else XATTN_ERR_INVALID_ARG); sink is one
+ * device uint32 that the kernel may overwrite with a meaningless value.
+ * bytes = 0 enqueues nothing.
+ */
+xattn_status xattn_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* xattn_status_string(xattn_status status);

@@ -5,8 +5,8 @@ TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 with the HIP library and imports nothing from it; it consumes the exact input
 values (bf16 or fp32, upcast exactly to float64) the device is given.
 
-What it computes (xGR page, "xGR: Efficient Generative Recommendation Serving at
-Scale", section 2.1 xAttention): every beam attends to the request's prompt
+What it computes (xGR page, "xGR: Atendimento de Recomendação Generativa
+Eficiente em Escala", section 2.1 xAttention): every beam attends to the request's prompt
 (the Shared cache, computed once at prefill) followed by the tokens generated
 along that beam's own history (the Non-Shared cache, one token per decode
 step). Splitting the computation into Shared / Non-Shared stages joined by an
@@ -114,30 +114,37 @@ def attention(w, *, include_prefix: bool = True, include_generated: bool = True,
 def attention_rows(w, rows, *, include_prefix=True, include_generated=True):
     """Decode attention for selected (beam n, query head q) pairs only.
 
-    Each row is computed on its own from the definition, so any row of a
-    full-size workload can be checked without the rest.
-    Returns O [len(rows), D], lse [len(rows)].
+    Every row gets the same single softmax over its own key sequence as in
+    ``attention``; rows of one (request, kv head) share one upcast of that
+    prompt's K/V and one call, so any rows of a full-size workload can be
+    checked without computing the rest. Rows may repeat and come in any
+    order. Returns O [len(rows), D], lse [len(rows)].
     """
     G = w.Hq // w.Hkv
     scale = float(np.float32(w.scale))
     O = np.empty((len(rows), w.D))
     LSE = np.empty(len(rows))
+    groups = {}
     for i, (n, qh) in enumerate(rows):
-        r, b = divmod(int(n), w.B)
-        h = int(qh) // G
+        groups.setdefault((int(n) // w.B, int(qh) // G), []).append(i)
+    for (r, h), idx in groups.items():
         P = int(w.prefix_len[r]) if include_prefix else 0
         L = int(w.unshared_len[r]) if include_generated else 0
         off = int(w.prefix_off[r])
         anc = lineage(w.parents, r, w.B, L)
         kp = _f64(w.k_shared[h, off:off + P])
         vp = _f64(w.v_shared[h, off:off + P])
-        src = [r * w.B + int(anc[t, b]) for t in range(L)]
-        kg = np.stack([_f64(w.k_new[t, src[t], h]) for t in range(L)])[None] if L else np.empty((1, 0, w.D))
-        vg = np.stack([_f64(w.v_new[t, src[t], h]) for t in range(L)])[None] if L else np.empty((1, 0, w.D))
-        qrow = _f64(w.q[int(n), int(qh)])[None, None]
-        o, lse = _attend_rows(qrow, kp, vp, kg, vg, scale)
-        O[i] = o[0, 0]
-        LSE[i] = lse[0, 0]
+        beams = [int(rows[i][0]) - r * w.B for i in idx]
+        qrows = np.stack([_f64(w.q[int(rows[i][0]), int(rows[i][1])]) for i in idx])[:, None, :]
+        kg = np.empty((len(idx), L, w.D))
+        vg = np.empty((len(idx), L, w.D))
+        for t in range(L):
+            src = r * w.B + anc[t, beams]
+            kg[:, t] = _f64(w.k_new[t, src, h])
+            vg[:, t] = _f64(w.v_new[t, src, h])
+        o, lse = _attend_rows(qrows, kp, vp, kg, vg, scale)
+        O[idx] = o[:, 0]
+        LSE[idx] = lse[:, 0]
     return O, LSE
 
 

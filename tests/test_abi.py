@@ -64,6 +64,11 @@ def _decode(d, ws=None, nbytes=0, **over):
     (dict(dtype=7), xattn.XATTN_ERR_UNSUPPORTED),
     (dict(max_unshared_len=0), xattn.XATTN_ERR_INVALID_ARG),
     (dict(scale=float("nan")), xattn.XATTN_ERR_INVALID_ARG),
+    (dict(scale=0.0), xattn.XATTN_ERR_INVALID_ARG),
+    (dict(scale=-0.1), xattn.XATTN_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), xattn.XATTN_ERR_INVALID_ARG),
+    (dict(scale=float("-inf")), xattn.XATTN_ERR_INVALID_ARG),
+    (dict(scale=3e38), xattn.XATTN_ERR_INVALID_ARG),   # scale * log2(e) overflows float32
     (dict(B=20000), xattn.XATTN_ERR_UNSUPPORTED),
     (dict(key_groups=3), xattn.XATTN_ERR_INVALID_ARG),
     (dict(key_groups=4, pipeline_stages=4), xattn.XATTN_ERR_INVALID_ARG),
@@ -213,3 +218,12 @@ def test_beam_topk_argument_checks(L):
     assert f(1, 8000, 8000, 4096, *P, None) == xattn.XATTN_ERR_UNSUPPORTED
     assert f(0, 4, 4, 4, *P, None) == xattn.XATTN_OK                     # nothing to do
     assert f(1, 4, 4, 0, *P, None) == xattn.XATTN_OK
+
+
+def test_stream_read_host_checks(L):
+    sink = FAKE
+    assert L.xattn_stream_read(None, 0, None, None) == xattn.XATTN_OK  # nothing to read
+    assert L.xattn_stream_read(None, 1024, sink, None) == xattn.XATTN_ERR_INVALID_ARG
+    assert L.xattn_stream_read(FAKE + 8, 1024, sink, None) == xattn.XATTN_ERR_INVALID_ARG
+    assert L.xattn_stream_read(FAKE, 1000, sink, None) == xattn.XATTN_ERR_INVALID_ARG
+    assert L.xattn_stream_read(FAKE, 1024, None, None) == xattn.XATTN_ERR_INVALID_ARG

@@ -59,6 +59,13 @@ CASES = {
     "no_prefix_bf16": dict(R=2, B=8, Hq=8, Hkv=2, D=128, prefix_len=[0, 0], unshared_len=[3, 2]),
     "no_gen_bf16": dict(R=2, B=8, Hq=8, Hkv=2, D=128, prefix_len=[200, 90], unshared_len=[0, 0], T_max=2),
     "long_gen_bf16": dict(R=2, B=4, Hq=8, Hkv=2, D=128, prefix_len=[300, 100], unshared_len=[70, 45]),
+    # generated tails longer than 16 tokens go to the vector kernel: every
+    # query-head grouping (1, 2, 4 of 4, 6 of 8, 8) and head dim 64 in bf16
+    "long_gen_d64_bf16": dict(R=2, B=3, Hq=4, Hkv=1, D=64, prefix_len=[130, 64], unshared_len=[40, 17]),
+    "long_gen_g1_bf16": dict(R=2, B=4, Hq=2, Hkv=2, D=128, prefix_len=[99, 0], unshared_len=[30, 20]),
+    "long_gen_g2_bf16": dict(R=1, B=5, Hq=4, Hkv=2, D=128, prefix_len=[300], unshared_len=[21]),
+    "long_gen_g6_bf16": dict(R=2, B=2, Hq=12, Hkv=2, D=128, prefix_len=[64, 131], unshared_len=[19, 33]),
+    "long_gen_g8_bf16": dict(R=1, B=4, Hq=16, Hkv=2, D=128, prefix_len=[200], unshared_len=[25]),
     "f32_small": dict(R=2, B=4, Hq=4, Hkv=1, D=64, prefix_len=[256, 100], unshared_len=[2, 3], dtype="f32"),
     "f32_d128": dict(R=1, B=3, Hq=8, Hkv=2, D=128, prefix_len=[190], unshared_len=[2], dtype="f32"),
 }
@@ -149,12 +156,58 @@ def test_decode_late_score_jump(rows, kg):
     compare(o, O, lse, L, "bf16", f"late score jump plan={plan}")
 
 
+@pytest.mark.parametrize("stage", ["unshared", "decode"])
+def test_vector_late_score_jump_generated(stage):
+    """Generated token 40 of a 70-token tail scores ~130 log2 units above
+    every other key, for every query row. The vector kernel's four key slots
+    take keys 4 apart, so only one slot sees it, after that slot's running
+    maximum was set by ten ordinary keys: that slot must rescale its
+    accumulated output by about 2^-127 (the lazy rescale's branch with a
+    finite maximum), and the slot combine must then give the other slots'
+    far smaller weights their due."""
+    w = make_workload("vjump", R=2, B=3, Hq=8, Hkv=2, D=128, prefix_len=[0, 150], unshared_len=[70, 70],
+                      seed_key=(313, 0))
+    w.q[:] = 0x3F80                    # bf16 1.0: a row's score is its key's row sum
+    w.k_new[40] = 0x4100               # bf16 8.0: score 1024 * scale for token 40 of every beam
+    w.k_new[40, :, :, :8] = 0x40E0     # slightly lower on a few elements: still the maximum by far
+    d = dv.upload(w)
+    dv.build_cache(d)
+    if stage == "unshared":
+        o, lse, ws, nb = dv.alloc_outputs(d, 1)
+        dv.unshared_stage(d, o, lse, ws, nb)
+        O, L = oa.attention(w, include_prefix=False)
+    else:
+        o, lse, ws, nb = dv.alloc_outputs(d, 2)
+        dv.decode(d, o, lse, ws, nb)
+        O, L = oa.attention(w)
+    torch.cuda.synchronize()
+    compare(_np(o)[:d.rows].reshape(O.shape), O, _np(lse)[:d.rows].reshape(L.shape), L, "bf16",
+            f"vector late score jump ({stage})")
+
+
+def test_vector_late_score_jump_f32_prompt():
+    """fp32 prompts run on the vector kernel: prompt key 40 of 300 (one key
+    slot) jumps ~130 log2 units above the rest after that slot has seen ten
+    keys; an fp32 generated tail follows."""
+    w = make_workload("vjump32", R=1, B=4, Hq=4, Hkv=1, D=64, prefix_len=[300], unshared_len=[3], dtype="f32",
+                      seed_key=(314, 0))
+    w.q[:] = 1.0
+    w.k_shared[:, 40, :] = 16.0        # score 1024 * scale
+    d, o, lse = run_decode(w)
+    plan = xattn.get_plan(d.dims, 2)
+    assert plan["mfma"] == 0, plan
+    O, L = oa.attention(w)
+    compare(o, O, lse, L, "f32", "fp32 vector late score jump")
+
+
 @pytest.mark.parametrize("name", ["ragged_small_bf16", "mfma_multi_tile", "b1_decode_bf16", "f32_small"])
 @pytest.mark.parametrize("ps", [0, 3])
 @pytest.mark.parametrize("kg", [0, 2])
 def test_shared_stage_matches_oracle(name, ps, kg):
-    if kg and (CASES[name].get("dtype") == "f32" or name == "b1_decode_bf16"):
-        pytest.skip("vector path: no key groups")
+    """Shared stage alone; single-beam bf16 prompts run on the MFMA kernel
+    too (a 32-row tile), with and without key groups and prompt splits."""
+    if kg and CASES[name].get("dtype") == "f32":
+        pytest.skip("fp32 prompts run on the vector kernel, which has no key groups")
     w = make_workload(name, seed_key=(302, ps), **CASES[name])
     d = dv.upload(w, prefix_splits=ps, key_groups=kg)
     o, lse, ws, nb = dv.alloc_outputs(d, 0)
@@ -165,7 +218,10 @@ def test_shared_stage_matches_oracle(name, ps, kg):
             f"shared {name}")
 
 
-@pytest.mark.parametrize("name", ["ragged_small_bf16", "long_gen_bf16", "b1_decode_bf16", "f32_small"])
+@pytest.mark.parametrize("name", ["ragged_small_bf16", "long_gen_bf16", "b1_decode_bf16", "f32_small",
+                                  "d64_bf16", "g1_bf16", "g6_bf16", "g8_bf16", "g16_bf16",
+                                  "long_gen_d64_bf16", "long_gen_g1_bf16", "long_gen_g2_bf16",
+                                  "long_gen_g6_bf16", "long_gen_g8_bf16"])
 @pytest.mark.parametrize("us", [0, 4])
 def test_unshared_stage_matches_oracle(name, us):
     w = make_workload(name, seed_key=(303, us), **CASES[name])

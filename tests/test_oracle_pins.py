@@ -269,7 +269,8 @@ def test_attention_rows_matches_full():
     w = make_workload("rows", R=2, B=4, Hq=8, Hkv=2, D=16, prefix_len=[30, 12], unshared_len=[3, 2],
                       seed_key=(109, 0), parent_dist="zipf")
     O, L = oa.attention(w)
-    rows = [(0, 0), (3, 7), (5, 2), (7, 5)]
+    # several rows of one (request, kv head), a repeat, and an unsorted order
+    rows = [(0, 0), (3, 7), (5, 2), (7, 5), (1, 1), (2, 3), (3, 7), (6, 0), (0, 6), (4, 4)]
     Or, Lr = oa.attention_rows(w, rows)
     for i, (n, q) in enumerate(rows):
         np.testing.assert_allclose(Or[i], O[n, q], atol=1e-13)
