@@ -17,12 +17,21 @@
 //    operand is read from row-major V in LDS with ds_read_b64_tr_b16.
 // K/V tiles (64 keys) move HBM -> LDS with buffer_load_dwordx4 ... lds (no
 // register staging), double-buffered so tile i+1 is in flight while tile i is
-// computed.
+// computed. With one key group, D = 128 and two stages, the walk over full
+// tiles is software-pipelined by 32-key halves (one half's S^T MFMAs beside
+// the previous half's softmax, its P.V beside the next half's row maximum),
+// and a stage's refill is split: the K rows of tile i+2 are issued as soon
+// as the first half of tile i has read its K, the V rows after the second
+// half; each refill is awaited with its own load count.
 //
-// Online softmax with a lazy rescale: the exponent offset only moves when a
-// tile's max exceeds it by more than 8 (log2 units), which keeps every
-// probability <= 256 and skips most output rescales; the result is exact
-// either way because the final division uses the same offset.
+// Online softmax with the exact running maximum as the exponent offset: the
+// output is rescaled whenever a half tile raises a row's maximum (the branch
+// is skipped when no row of the wave moves). The probabilities are rounded
+// to bf16 for the P.V MFMAs, so the offset is kept exact rather than lazy:
+// with an offset up to 8 (log2) below the maximum, the dominant key's weight
+// 2^x is rounded too, and rows where one key carries most of the weight (V
+// entries of up to ~30 in the outlier workloads) lost up to ~3e-2 absolute;
+// with the exact maximum that key's weight is exactly 1.
 //
 // Non-Shared part (prompt split 0, or a member of its own, when fused): the
 // beam's own generated tokens, gathered through its slot-table row, join the
@@ -36,6 +45,8 @@
 // counter that returns to zero - merges all partials with the log-sum-exp
 // rule and writes the final output. In mode PARTIAL each split only writes its
 // partial slot for a later reduction.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -157,6 +168,27 @@ __device__ __forceinline__ float xor32(float x) {
   return __builtin_bit_cast(float, (__lane_id() & 32) ? w[0] : w[1]);
 }
 
+// Maximum / sum of a value over the two lane halves (lanes c and c + 32), in
+// every lane: the lane swap of two copies leaves [lo | lo] in one and
+// [hi | hi] in the other, so one max or add combines them (no select). The
+// two results are copied out of the swap's vector into scalars before the
+// bit casts: a bit cast applied to an element of that vector directly was
+// measured to read element 0 for both.
+__device__ __forceinline__ float max_halves(float x) {
+  const unsigned a = __builtin_bit_cast(unsigned, x);
+  const auto w = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  const unsigned w0 = w[0];
+  const unsigned w1 = w[1];
+  return fmaxf(__builtin_bit_cast(float, w0), __builtin_bit_cast(float, w1));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const unsigned a = __builtin_bit_cast(unsigned, x);
+  const auto w = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  const unsigned w0 = w[0];
+  const unsigned w1 = w[1];
+  return __builtin_bit_cast(float, w0) + __builtin_bit_cast(float, w1);
+}
+
 // Online-softmax update for one 32-key half of a tile (S^T block `sb`, the
 // 16 scores this lane holds for its query column), followed by that half's
 // P.V MFMAs. Processing the halves separately lets the vector-ALU softmax of
@@ -178,8 +210,8 @@ __device__ __forceinline__ void half_softmax_pv(const char* buf, int vbase, f32x
 #pragma unroll
   for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sb[i]), sb[i + 1]);
   mx = fmaxf(mx, sb[15]);
-  mx = fmaxf(mx, xor32(mx)) * c;
-  if (__any(mx > m_run + 8.0f)) {
+  mx = max_halves(mx) * c;
+  if (__any(mx > m_run)) {
     const float mn = fmaxf(m_run, mx);
     const float alpha = exp2_approx(m_run - mn);
 #pragma unroll
@@ -310,6 +342,133 @@ __device__ __forceinline__ void token_block_step(const char* blk, const bf16x8_t
   half_softmax_pv<D, false, true>(blk + 24 * TG::ROWB - TG::TILEB, vbase, sacc, 0, oacc, m_run, l_part, c, hh, BN);
 }
 
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// A buffer descriptor (base, no stride, num_records bytes, the same format
+// word as the loads' other descriptors) as four scalar words.
+__device__ __forceinline__ i32x4_t raw_rsrc_words(const void* base, int num_records) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4_t{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), num_records, 0x00020000};
+}
+
+// One direct HBM -> LDS load of 16 bytes per lane (buffer_load_dwordx4 with
+// the lds bit) to LDS byte address `lds` (uniform), written as inline
+// assembly: the compiler's wait insertion cannot tell which LDS range such a
+// load writes and would wait for every one in flight before each LDS read
+// of the other stage. The pipelined walk waits for these loads itself
+// (vmcnt) and publishes them with a barrier. No register is written.
+__device__ __forceinline__ void lds_dma16(i32x4_t rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   :
+                   : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                   : "memory", "m0");
+}
+
+// ---- Software-pipelined walk over full 64-key tiles (one key group) ----
+//
+// A wavefront works through 32-key halves. Half h's S^T MFMAs are issued
+// while the probabilities of half h-1 are formed on the vector ALU (scale,
+// exp2, bf16 packing, row sum), and half h-1's P.V MFMAs run while half h's
+// row maxima are taken; the rescale branch of half h follows the P.V
+// MFMAs of half h-1, so the output it rescales holds every earlier half and
+// half h's probabilities use the updated offset. Every basic block between
+// two branches thus pairs 8 MFMAs (256 cycles of the matrix core) with the
+// vector work of another half, which one wavefront issues in their shadow.
+
+// K operands of one 32-key half (kb) of the tile at buf.
+template <int D>
+__device__ __forceinline__ void read_k_half(const char* buf, int kbase, int kb, bf16x8_t* ka) {
+  using TG = TileGeom<D>;
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc)
+    ka[dc] = *reinterpret_cast<const bf16x8_t*>(buf + (kbase ^ (32 * dc)) + kb * 32 * TG::ROWB);
+}
+
+// S^T of one half on the matrix cores (the first MFMA starts from zero).
+template <int D>
+__device__ __forceinline__ f32x16_t s_half(const bf16x8_t* ka, const bf16x8_t* qf) {
+  f32x16_t sacc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc], qf[dc], sacc, 0, 0, 0);
+  return sacc;
+}
+
+// Probabilities of one half (raw scores sc, offset m), packed to bf16 for
+// the P.V MFMAs, and their running sum.
+__device__ __forceinline__ void probs_half(const f32x16_t& sc, float c, float m, bf16x8_t* pf, float& l) {
+  float lsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float p = exp2_approx(__builtin_fmaf(sc[i], c, -m));
+    lsum += p;
+    pf[i >> 3][i & 7] = (__bf16)p;
+  }
+  l += lsum;
+}
+
+// Raw row maximum of one half's scores over both lane halves.
+__device__ __forceinline__ float rowmax_half(const f32x16_t& sc) {
+  float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sc[i]), sc[i + 1]);
+  return max_halves(fmaxf(mx, sc[15]));
+}
+
+// O^T += V^T . P^T for one half (kb) of the tile at buf.
+template <int D>
+__device__ __forceinline__ void pv_half(const char* buf, int vbase, int kb, const bf16x8_t* pf, f32x16_t* oacc) {
+  using TG = TileGeom<D>;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      const int vo = (vbase ^ (64 * db)) + (16 * (2 * kb + ch)) * TG::ROWB;
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(buf + vo));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(buf + vo + 8 * TG::ROWB));
+      const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ch], oacc[db], 0, 0, 0);
+    }
+}
+
+// One pipelined half-step's first block: the next half's S^T MFMAs (sn)
+// interleaved with the current half's probabilities.
+// The K operands are read here, two MFMAs ahead of their use, so that only a
+// few of them occupy registers at a time.
+template <int D>
+__device__ __forceinline__ void pipe_s_probs(const char* kbuf, int kbase, int kb, const bf16x8_t* qf, f32x16_t& sn,
+                                             const f32x16_t& sc, float c, float m, bf16x8_t* pf, float& l) {
+  bf16x8_t ka[D / 16];
+  read_k_half<D>(kbuf, kbase, kb, ka);
+  sn = s_half<D>(ka, qf);
+  probs_half(sc, c, m, pf, l);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // the first two K reads
+#pragma unroll
+  for (int k = 0; k < D / 16; ++k) {
+    if (k + 2 < D / 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the read two MFMAs ahead
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then six vector instructions
+  }
+}
+
+// Its second block: the current half's P.V MFMAs (V^T read from LDS beside
+// them) interleaved with the next half's row maximum.
+template <int D>
+__device__ __forceinline__ float pipe_pv_max(const char* buf, int vbase, int kb, const bf16x8_t* pf, f32x16_t* oacc,
+                                             const f32x16_t& sn) {
+  pv_half<D>(buf, vbase, kb, pf, oacc);
+  const float mx = rowmax_half(sn);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the first V^T reads
+#pragma unroll
+  for (int k = 0; k < D / 16; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+  }
+  return mx;
+}
+
 // Wait until at most n vector-memory operations are in flight. The counter
 // field needs an immediate (at most 63), so n is rounded down to a multiple
 // of 8 (a smaller count only waits longer).
@@ -323,6 +482,17 @@ __device__ __forceinline__ void wait_vm_at_most(int n) {
   else if (n >= 16) __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
   else if (n >= 8) __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
   else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Wait until at most N (if keep) or no vector-memory operations are in
+// flight (keep is uniform).
+template <int N>
+__device__ __forceinline__ void wait_vm_keep(bool keep) {
+  static_assert(N >= 0 && N <= 63, "vmcnt field");
+  if (keep)
+    __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  else
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Wait until at most `ahead` tiles' loads (each `lpt` instructions per wave)
@@ -498,7 +668,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS addresses stay scalar
   const int kg = __builtin_amdgcn_readfirstlane(wave / RG);
   const int rg = wave - kg * RG;
   const int hh = lane >> 5;
@@ -530,6 +700,9 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   // the loop, the first slot cell already in hand.
   constexpr int NPF = (NS * SBUF > 80 * 1024 && NW <= 4) ? 2 : 0;
   constexpr int NSL = NPF > 0 ? NPF : 1;
+  // One key group, head dim 128, two stages: the full tiles go through the
+  // software-pipelined walk.
+  constexpr bool PIPE = D == 128 && KG == 1 && NS == 2 && !TB && NPF == 0;
   int zv;
   __asm__ volatile("v_mov_b32 %0, 0" : "=v"(zv));
   const int Pv = a.prefix_len[r + zv];
@@ -606,7 +779,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   auto issue_part = [&](int t, bool do_k, bool do_v) {
     lds_char* buf = lsm + (t % NS) * SBUF + wave * 1024;
     const int pt = t < nsup - 1 ? (t + rot) % (nsup - 1) : t;  // super-tile loaded at step t
-    const uint32_t tile_bytes = (uint32_t)((kbeg + pt * ST) * TG::ROWB);
+    // (uniform: kept in a scalar register, the loads' scalar offset)
+    const uint32_t tile_bytes = __builtin_amdgcn_readfirstlane((uint32_t)((kbeg + pt * ST) * TG::ROWB));
 #pragma unroll
     for (int j = 0; j < LP::NJ; ++j) {
       if (do_k) __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, buf + LP::lds_off(j), 16, lp.k[j], tile_bytes, 0, 0);
@@ -615,15 +789,38 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
     }
   };
   auto issue_tile = [&](int t) { issue_part(t, true, true); };
+  // The pipelined walk refills the K and V halves of a stage separately and
+  // through lds_dma16 (all K loads of a tile, then all V loads, so that
+  // vmcnt counts them in that order).
+  const i32x4_t rk_w = raw_rsrc_words(Kg, prompt_bytes);
+  const i32x4_t rv_w = raw_rsrc_words(Vg, prompt_bytes);
+  auto issue_asm = [&](int t, bool is_v) {  // full tile t (no rotation with one key group)
+    const uint32_t base = (uint32_t)(uintptr_t)lsm + (uint32_t)((t % NS) * SBUF + wave * 1024 + (is_v ? TG::TILEB : 0));
+    const uint32_t tile_bytes = __builtin_amdgcn_readfirstlane((uint32_t)((kbeg + t * ST) * TG::ROWB));
+#pragma unroll
+    for (int j = 0; j < LP::NJ; ++j)
+      lds_dma16(is_v ? rv_w : rk_w, __builtin_amdgcn_readfirstlane(base + LP::lds_off(j)), is_v ? lp.v[j] : lp.k[j],
+                tile_bytes);
+  };
   NonShared<D, KG> ns;
   ns.L = early_slots ? __builtin_amdgcn_readfirstlane(lenv) : 0;  // the fused append sets it below
   ns.kg = kg;
   ns.tnew = -1;
   ns.hkv = s.Hkv;
-  ns.kp = do_ns ? a.k_pool + (int64_t)h * D + 8 * hh : a.q;
-  ns.vp = do_ns ? a.v_pool + (int64_t)h * D + 4 * hh : a.q;
-  ns.knew = ns.kp;
-  ns.vnew = ns.vp;
+  // The per-lane row pointers are set where the tokens are fetched (after
+  // the prompt loop with the pipelined walk, whose registers are tight).
+  auto set_row_ptrs = [&]() {
+    ns.kp = do_ns ? a.k_pool + (int64_t)h * D + 8 * hh : a.q;
+    ns.vp = do_ns ? a.v_pool + (int64_t)h * D + 4 * hh : a.q;
+    ns.knew = ns.kp;
+    ns.vnew = ns.vp;
+    if (app) {  // uniform
+      const int64_t nrow = (((int64_t)r * s.B + bq) * s.Hkv + h) * D;
+      ns.knew = a.k_new + nrow + 8 * hh;
+      ns.vnew = a.v_new + nrow + 4 * hh;
+    }
+  };
+  if constexpr (!PIPE) set_row_ptrs();
   ns.trow = trow;
   uint4 pk[NPF > 0 ? NPF : 1][NDC];
   uint2 pv[NPF > 0 ? NPF : 1][NDB][4];
@@ -679,9 +876,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
       cpv = *reinterpret_cast<const uint4*>((pc < D / 8 ? a.k_new : a.v_new) +
                                             (((int64_t)r * s.B + b_lo + bl) * s.Hkv + h) * D + 8 * (pc % (D / 8)));
     }
-    const int64_t nrow = (((int64_t)r * s.B + bq) * s.Hkv + h) * D;
-    ns.knew = a.k_new + nrow + 8 * hh;
-    ns.vnew = a.v_new + nrow + 4 * hh;
+    if constexpr (!PIPE) set_row_ptrs();
 #pragma unroll
     for (int u = 0; u < NSL; ++u) pslot[u] = ns.slot(u);
   }
@@ -793,6 +988,108 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   auto issue_v = [&]() {
     if (v_pending >= 0) issue_part(v_pending, false, true);
   };
+  if constexpr (PIPE) {
+    // Full tiles through the pipelined walk. Tile t sits at stage t % 2; the
+    // loads of tile t + 1 are waited for (and made visible by a barrier)
+    // before its first S^T MFMAs, and tile t + 2 is requested into stage
+    // t % 2 once every wave has read tile t (a second barrier). A partial
+    // last tile is requested only after the walk and goes through the
+    // masked step. Every tile runs the same code: the last full tile's
+    // look-ahead S^T reads the other stage, which then holds the tile before
+    // it (keys already seen, so its row maximum never moves the offset) and
+    // whose result is dropped; one code path keeps the loop free of the
+    // register copies a join of two paths costs.
+    const int nfull = nkeys / BN;
+    const bool pipe = nfull >= 2;  // uniform
+    if (pipe) {
+      const float inv_c = 1.0f / c;
+      float thr = m_run * inv_c;  // raw score above which the offset moves
+      auto rescale = [&](float mx) {
+        if (__any(mx > thr)) {  // uniform; rare after the first half
+          const float mn = fmaxf(m_run, mx * c);
+          const float alpha = exp2_approx(m_run - mn);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+          l_part *= alpha;
+          m_run = mn;
+          thr = mn * inv_c;
+        }
+      };
+      wait_vmem();
+      __syncthreads();  // tile 0 landed for every wave
+      issue_asm(1, false);  // a full tile (nfull >= 2): K, then V
+      issue_asm(1, true);
+      issued = 2;
+      bf16x8_t pf[2];
+      f32x16_t sc, sn;
+      {
+        bf16x8_t ka[NDC];
+        read_k_half<D>(smem, kbase, 0, ka);
+        sc = s_half<D>(ka, qf);
+      }
+      rescale(rowmax_half(sc));
+      // Refills: K of tile t + 2 goes out once every wave has read K of tile
+      // t (mid-tile), V of tile t + 2 once every wave has read V of tile t
+      // (end of tile); each wait leaves the one younger group in flight.
+      int t = 0;
+      auto body = [&](auto stage_c) {
+        constexpr int S = decltype(stage_c)::value;
+        const char* buf = smem + S * SBUF;
+        const bool next = t + 1 < nfull, next2 = t + 2 < nfull;  // uniform
+        // half 0 of tile t: S^T of half 1 beside the probabilities of half 0
+        pipe_s_probs<D>(buf, kbase, 1, qf, sn, sc, c, m_run, pf, l_part);
+        float mx = pipe_pv_max<D>(buf, vbase, 0, pf, oacc, sn);
+        rescale(mx);
+        sc = sn;
+        // K of tile t + 1 landed (its V may still be in flight)
+        wait_vm_keep<LP::NJ>(next);
+        __syncthreads();
+        if (next2) issue_asm(t + 2, false);
+        // half 1: S^T of the next tile's first half (the other stage; for
+        // the last tile that stage holds keys already seen, result dropped)
+        pipe_s_probs<D>(smem + (S ^ 1) * SBUF, kbase, 0, qf, sn, sc, c, m_run, pf, l_part);
+        mx = pipe_pv_max<D>(buf, vbase, 1, pf, oacc, sn);
+        // V of tile t + 1 landed (K of tile t + 2 may still be in flight)
+        wait_vm_keep<LP::NJ>(next2);
+        __syncthreads();
+        if (next2) {
+          issue_asm(t + 2, true);
+          issued = t + 3;
+        }
+        rescale(mx);
+        sc = sn;
+        ++t;
+      };
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      while (t + 1 < nfull) {
+        body(I0{});
+        body(I1{});
+      }
+      if (t < nfull) body(I0{});
+    }
+    // Without two full tiles, or for the partial last tile: the masked step
+    // (its loads requested now when the walk left them out).
+    for (int it = pipe ? nfull : 0; it < nsup; ++it) {
+      if (pipe && issued <= it) {
+        issue_tile(it);
+        issued = it + 1;
+      }
+      advance(it);
+      const int nv = min(nkeys - it * BN, BN);
+      const char* buf = smem + (it % NS) * SBUF;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {  // one half at a time: few registers
+        if (nv <= 32 * kb) break;  // uniform
+        bf16x8_t ka[NDC];
+        read_k_half<D>(buf, kbase, kb, ka);
+        f32x16_t sacc = s_half<D>(ka, qf);
+        half_softmax_pv<D, true>(buf, vbase, sacc, kb, oacc, m_run, l_part, c, hh, nv);
+      }
+    }
+  } else {
   // This wave's tile of super-tile `it` sits at stage (it % NS), slot kg.
   for (int it = 0; it + 1 < nsup; ++it) {  // full super-tiles
     advance(it);
@@ -825,6 +1122,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
                            hh, min(nv, BN));
     }
   }
+  }  // !PIPE
+  if constexpr (PIPE) set_row_ptrs();
 
   if (nsup == 0) issue_tok();
   wait_vmem();  // every tile load has landed before the stage buffers are reused
@@ -906,7 +1205,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
       a.ulen_rw[r] = grow ? t_app + 1 : t_app;
   }
 
-  float l_tot = l_part + xor32(l_part);
+  float l_tot = sum_halves(l_part);
   // own[j]: column block kg*NDBW + j of this wave's 32 rows, combined over
   // the key groups. Each group hands every other group the column blocks
   // that group finalizes (KG - 1 slots per block), then merges the ones it
