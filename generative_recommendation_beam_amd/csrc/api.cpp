@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "xattn.h"
 #include "kernels.h"
@@ -605,6 +606,67 @@ xattn_status xattn_append_decode(const xattn_dims* d, const void* q, const void*
   const Workspace w{static_cast<unsigned*>(ws), nullptr, nullptr};
   return hip_status(run_prefix(d, p, kModeFinal, q, ks, vs, poff, plen, kp, vp, table_in, ulen,
                                OutSpec{o, lse, 0, 0}, w, st, &fa));
+}
+
+}  // extern "C"
+
+// ---- xattn_append_decode_static: the workspace in a device-resident array ----
+namespace {
+
+// The largest workspace the allocation-free entry point serves: the folded
+// append needs R*H_kv counters; unfolded plans (long generated tails, split
+// prompts) also need their partial outputs.
+constexpr size_t kStaticWorkspaceBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+
+// One copy per GPU, alive until the process ends. In host code this name is
+// only a handle for hipGetSymbolAddress: kernels and copies take the device
+// address it returns (static_ws_ptr[dev]).
+__device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
+
+void* static_ws_ptr[kMaxDevices];
+hipError_t static_ws_err[kMaxDevices];
+std::once_flag static_ws_once[kMaxDevices];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(unsigned* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
+}  // namespace
+
+extern "C" {
+
+xattn_status xattn_append_decode_static(const xattn_dims* d, const void* q, const void* ks, const void* vs,
+                                        const int64_t* poff, const int32_t* plen, const void* k_new,
+                                        const void* v_new, const int32_t* parent, const int64_t* slot_base,
+                                        const uint8_t* active, void* kp, void* vp, const int32_t* table_in,
+                                        int32_t* table_out, int32_t* ulen, float* o, float* lse, void* stream) {
+  xattn_status e = check_dims(d);
+  if (e != XATTN_OK) return e;
+  const Plan p = make_plan(d, 2);
+  const Layout L = layout_for(d, p, 3);
+  if (L.total > kStaticWorkspaceBytes) return XATTN_ERR_WORKSPACE;  // beyond the fixed array
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return XATTN_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return XATTN_ERR_UNSUPPORTED;
+  std::call_once(static_ws_once[dev], [dev] {
+    static_ws_err[dev] = hipGetSymbolAddress(&static_ws_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (static_ws_err[dev] != hipSuccess || static_ws_ptr[dev] == nullptr) return XATTN_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // The split counters at the head of the workspace must be zero; the array
+  // keeps whatever the last call left, so they are cleared here (a fill
+  // kernel, not a memset node, so that a captured graph replays it cleanly).
+  const size_t ctr_bytes = L.o > 0 ? L.o : L.total;
+  if (ctr_bytes > 0) {
+    const int64_t words = (int64_t)(ctr_bytes / 4);
+    const unsigned grid = (unsigned)std::min<int64_t>(std::max<int64_t>((words + 255) / 256, 1), 1024);
+    hipLaunchKernelGGL(zero_words_kernel, dim3(grid), dim3(256), 0, st, static_cast<unsigned*>(static_ws_ptr[dev]),
+                       words);
+    if (hipGetLastError() != hipSuccess) return XATTN_ERR_HIP;
+  }
+  return xattn_append_decode(d, q, ks, vs, poff, plen, k_new, v_new, parent, slot_base, active, kp, vp, table_in,
+                             table_out, ulen, o, lse, static_ws_ptr[dev], L.total, stream);
 }
 
 static size_t paged_ws_bytes(const xattn_dims* d, int32_t max_seq_len) {

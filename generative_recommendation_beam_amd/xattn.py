@@ -24,7 +24,7 @@ EXPORTED = ("xattn_workspace_size", "xattn_get_plan", "xattn_shared_stage", "xat
             "xattn_paged_workspace_size", "xattn_paged_decode", "xattn_paged_copy_blocks",
             "xattn_cht_create", "xattn_cht_destroy", "xattn_cht_insert", "xattn_cht_best",
             "xattn_cht_admit", "xattn_cht_complete", "xattn_cht_form_batch", "xattn_step_graph_create",
-            "xattn_step_graph_launch", "xattn_step_graph_destroy", "xattn_stream_read",
+            "xattn_step_graph_launch", "xattn_step_graph_destroy", "xattn_stream_read", "xattn_append_decode_static",
             "xattn_status_string")
 
 
@@ -143,6 +143,8 @@ def lib():
     L.xattn_step_graph_launch.argtypes = [P, P]
     L.xattn_step_graph_destroy.restype = ctypes.c_int
     L.xattn_step_graph_destroy.argtypes = [P]
+    L.xattn_append_decode_static.restype = ctypes.c_int
+    L.xattn_append_decode_static.argtypes = [pd] + [P] * 17 + [P]
     L.xattn_stream_read.restype = ctypes.c_int
     L.xattn_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
     _lib = L
@@ -252,6 +254,18 @@ def stream_read(src, sink, nbytes=None, stream=None):
     """Measurement utility: read `nbytes` (default: all) of tensor src once."""
     nbytes = src.numel() * src.element_size() if nbytes is None else int(nbytes)
     _check(lib().xattn_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "xattn_stream_read")
+
+
+def append_decode_static(dims, q, k_shared, v_shared, prefix_off, prefix_len, k_new, v_new, parent, slot_base,
+                         active, k_pool, v_pool, table_in, table_out, unshared_len, o, lse=None, stream=None):
+    """xattn_append_decode with the library's fixed device workspace (no
+    workspace argument; calls on one GPU must not overlap)."""
+    _check(lib().xattn_append_decode_static(ctypes.byref(dims), _ptr(q), _ptr(k_shared), _ptr(v_shared),
+                                            _ptr(prefix_off), _ptr(prefix_len), _ptr(k_new), _ptr(v_new),
+                                            _ptr(parent), _ptr(slot_base), _ptr(active), _ptr(k_pool),
+                                            _ptr(v_pool), _ptr(table_in), _ptr(table_out), _ptr(unshared_len),
+                                            _ptr(o), _ptr(lse), _stream(stream)),
+           "xattn_append_decode_static")
 
 
 def paged_workspace_size(dims, max_seq_len) -> int:

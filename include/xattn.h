@@ -248,6 +248,29 @@ xattn_status xattn_append_decode(const xattn_dims* dims, const void* q, const vo
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * xattn_append_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, which comes instead
+ * from a fixed array of 32 MiB in the library's device memory (one per GPU,
+ * held until the process ends; found once per device on the first call).
+ * Nothing is allocated or freed. The split counters at its head are cleared
+ * by a small fill kernel on `stream` before the call's own launch.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on a
+ * GPU (different streams, threads) race and must not be issued. Results are
+ * those of xattn_append_decode with a workspace of xattn_workspace_size(dims,
+ * 3) bytes. XATTN_ERR_WORKSPACE if that size exceeds 32 MiB; otherwise the
+ * errors of xattn_append_decode, and XATTN_ERR_HIP if the array's address
+ * cannot be found.
+ */
+xattn_status xattn_append_decode_static(const xattn_dims* dims, const void* q, const void* k_shared,
+                                        const void* v_shared, const int64_t* prefix_off,
+                                        const int32_t* prefix_len, const void* k_new, const void* v_new,
+                                        const int32_t* parent, const int64_t* slot_base,
+                                        const uint8_t* active, void* k_pool, void* v_pool,
+                                        const int32_t* table_in, int32_t* table_out,
+                                        int32_t* unshared_len, float* o, float* lse, void* stream);
+
+/*
  * Beam-search survivor selection for one decode step (xGR page, section 2.2
  * xBeam: the Top-K sequences are chosen from the pool of every live beam's
  * candidates; since a beam's candidates come sorted, a walk over the pool
