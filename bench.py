@@ -585,6 +585,11 @@ def main():
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the PagedAttention-style baseline measured beside the step")
     ap.add_argument("--no-stream", action="store_true", help="skip the streaming-read bandwidth")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run one plain device-to-device copy of BYTES (the reference kernel "
+                         "the HBM byte counters are scaled by) and exit")
+    ap.add_argument("--profile-steps", type=int, default=0, metavar="N",
+                    help="only build the workload and run N eager steps (for counter collection), then exit")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from the host instead of one captured step graph")
     args = ap.parse_args()
@@ -601,7 +606,28 @@ def main():
         raise SystemExit(f"bench.py: {xattn.LIB_PATH} is not built (run __graft_entry__.build())")
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = args.calibrate_copy // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4}), flush=True)
+        return
     cfg = _cfg_key(args.config)
+    if args.profile_steps:
+        # Counter collection: the workload's calls only, eagerly (every
+        # dispatch after the first beam selection belongs to a step).
+        args.eager = True
+        s = Setup(cfg, args.layers or DEFAULT_LAYERS[str(cfg)], args)
+        for _ in range(args.profile_steps):
+            s.one_step()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps, "config": WORKLOAD_NAMES[str(cfg)],
+                          "n_layers": s.n_layers, "plan": s.plan, "kernel_hash": kernel_hash()}), flush=True)
+        s.close()
+        return
     extras = args.extra_configs
     if extras is None:
         extras = "2" if str(cfg) == DEFAULT_CONFIG else ""
