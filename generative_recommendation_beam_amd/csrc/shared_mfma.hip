@@ -369,11 +369,11 @@ __device__ __forceinline__ void lds_dma16(i32x4_t rsrc, uint32_t lds, uint32_t v
 // A wavefront works through 32-key halves. Half h's S^T MFMAs are issued
 // while the probabilities of half h-1 are formed on the vector ALU (scale,
 // exp2, bf16 packing, row sum), and half h-1's P.V MFMAs run while half h's
-// row maxima are taken; the rescale branch of half h follows the P.V
-// MFMAs of half h-1, so the output it rescales holds every earlier half and
-// half h's probabilities use the updated offset. Every basic block between
-// two branches thus pairs 8 MFMAs (256 cycles of the matrix core) with the
-// vector work of another half, which one wavefront issues in their shadow.
+// row maxima are taken. Half h's rescale branch is taken after the first
+// S^T MFMAs of half h+1 are issued (they do not depend on it), so the matrix
+// core has work while the wave resolves the branch; the output it rescales
+// holds every half up to h-1, and half h's probabilities, formed next, use
+// the updated offset.
 
 // K operands of one 32-key half (kb) of the tile at buf.
 template <int D>
@@ -432,39 +432,53 @@ __device__ __forceinline__ void pv_half(const char* buf, int vbase, int kb, cons
     }
 }
 
-// One pipelined half-step's first block: the next half's S^T MFMAs (sn)
-// interleaved with the current half's probabilities.
-// The K operands are read here, two MFMAs ahead of their use, so that only a
-// few of them occupy registers at a time.
-template <int D>
-__device__ __forceinline__ void pipe_s_probs(const char* kbuf, int kbase, int kb, const bf16x8_t* qf, f32x16_t& sn,
-                                             const f32x16_t& sc, float c, float m, bf16x8_t* pf, float& l) {
+// S^T of the next half with the pending rescale decision taken after its
+// first MFMAs are issued (they do not depend on it), then the rest of S^T
+// beside the probabilities of the current half at the updated offset.
+template <int D, typename RS>
+__device__ __forceinline__ void pipe_s_rescale_probs(const char* kbuf, int kbase, int kb, const bf16x8_t* qf,
+                                                     f32x16_t& sn, const f32x16_t& sc, float c, const float& m,
+                                                     bf16x8_t* pf, float& l, RS&& rescale, float mx) {
   bf16x8_t ka[D / 16];
   read_k_half<D>(kbuf, kbase, kb, ka);
-  sn = s_half<D>(ka, qf);
-  probs_half(sc, c, m, pf, l);
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // the first two K reads
+  f32x16_t acc;
 #pragma unroll
-  for (int k = 0; k < D / 16; ++k) {
-    if (k + 2 < D / 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the read two MFMAs ahead
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then six vector instructions
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1], qf[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[2], qf[2], acc, 0, 0, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  rescale(mx);
+#pragma unroll
+  for (int dc = 3; dc < D / 16; ++dc) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc], qf[dc], acc, 0, 0, 0);
+  probs_half(sc, c, m, pf, l);
+  sn = acc;
+#pragma unroll
+  for (int k = 3; k < D / 16; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
   }
 }
 
-// Its second block: the current half's P.V MFMAs (V^T read from LDS beside
-// them) interleaved with the next half's row maximum.
+// P.V of the current half with its V^T reads, then the row maximum of the
+// next half's scores (ready by then).
 template <int D>
-__device__ __forceinline__ float pipe_pv_max(const char* buf, int vbase, int kb, const bf16x8_t* pf, f32x16_t* oacc,
-                                             const f32x16_t& sn) {
+__device__ __forceinline__ float pipe_pv_then_max(const char* buf, int vbase, int kb, const bf16x8_t* pf,
+                                                  f32x16_t* oacc, const f32x16_t& sn) {
   pv_half<D>(buf, vbase, kb, pf, oacc);
   const float mx = rowmax_half(sn);
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the first V^T reads
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
   for (int k = 0; k < D / 16; ++k) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    if (k >= 2) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
   }
   return mx;
 }
@@ -1029,7 +1043,10 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
         read_k_half<D>(smem, kbase, 0, ka);
         sc = s_half<D>(ka, qf);
       }
-      rescale(rowmax_half(sc));
+      // The rescale decision of each half is applied at the start of the
+      // next step (after its first S^T MFMAs); the last one, of the dropped
+      // look-ahead, is dropped with it.
+      float mxp = rowmax_half(sc);
       // Refills: K of tile t + 2 goes out once every wave has read K of tile
       // t (mid-tile), V of tile t + 2 once every wave has read V of tile t
       // (end of tile); each wait leaves the one younger group in flight.
@@ -1038,10 +1055,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
         constexpr int S = decltype(stage_c)::value;
         const char* buf = smem + S * SBUF;
         const bool next = t + 1 < nfull, next2 = t + 2 < nfull;  // uniform
-        // half 0 of tile t: S^T of half 1 beside the probabilities of half 0
-        pipe_s_probs<D>(buf, kbase, 1, qf, sn, sc, c, m_run, pf, l_part);
-        float mx = pipe_pv_max<D>(buf, vbase, 0, pf, oacc, sn);
-        rescale(mx);
+        pipe_s_rescale_probs<D>(buf, kbase, 1, qf, sn, sc, c, m_run, pf, l_part, rescale, mxp);
+        mxp = pipe_pv_then_max<D>(buf, vbase, 0, pf, oacc, sn);
         sc = sn;
         // K of tile t + 1 landed (its V may still be in flight)
         wait_vm_keep<LP::NJ>(next);
@@ -1049,8 +1064,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
         if (next2) issue_asm(t + 2, false);
         // half 1: S^T of the next tile's first half (the other stage; for
         // the last tile that stage holds keys already seen, result dropped)
-        pipe_s_probs<D>(smem + (S ^ 1) * SBUF, kbase, 0, qf, sn, sc, c, m_run, pf, l_part);
-        mx = pipe_pv_max<D>(buf, vbase, 1, pf, oacc, sn);
+        pipe_s_rescale_probs<D>(smem + (S ^ 1) * SBUF, kbase, 0, qf, sn, sc, c, m_run, pf, l_part, rescale, mxp);
+        mxp = pipe_pv_then_max<D>(buf, vbase, 1, pf, oacc, sn);
         // V of tile t + 1 landed (K of tile t + 2 may still be in flight)
         wait_vm_keep<LP::NJ>(next2);
         __syncthreads();
@@ -1058,7 +1073,6 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
           issue_asm(t + 2, true);
           issued = t + 3;
         }
-        rescale(mx);
         sc = sn;
         ++t;
       };

@@ -25,7 +25,12 @@ LAYERS = [
     dict(R=3, B=8, Hq=4, Hkv=1, D=64, prefix_len=[130, 0, 64], unshared_len=[2, 1, 3]),
     dict(R=2, B=40, Hq=16, Hkv=4, D=128, prefix_len=[700, 1100], unshared_len=[1, 4]),
     dict(R=1, B=4, Hq=4, Hkv=1, D=64, prefix_len=[256], unshared_len=[2], dtype="f32"),
+    # long generated tails: the prompt pass, a Non-Shared pass of its own and
+    # the Merge, all captured
+    dict(R=2, B=4, Hq=8, Hkv=2, D=128, prefix_len=[600, 300], unshared_len=[40, 20]),
+    dict(R=2, B=3, Hq=4, Hkv=1, D=64, prefix_len=[0, 150], unshared_len=[30, 25]),
 ]
+LONG_TAIL = [4, 5]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -89,14 +94,19 @@ def test_step_graph_every_replay_matches_oracle():
         g.close()
 
 
-def test_step_graph_equals_eager_bitwise():
-    """A replay gives the same bits as the eager calls it captured."""
-    kw = LAYERS[0]
-    w = make_workload("stepE", seed_key=(321, 0), **kw)
+@pytest.mark.parametrize("li", [0] + LONG_TAIL)
+def test_step_graph_equals_eager_bitwise(li):
+    """A replay gives the same bits as the eager calls it captured (for the
+    long tails: three launches per layer)."""
+    kw = LAYERS[li]
+    w = make_workload("stepE", seed_key=(321, li), **kw)
     d = dv.upload(w)
     table_in, table_out, t_last = dv.prepare_step(d)
     u0 = d.unshared_len.clone()
     o, lse, ws, nb = dv.alloc_outputs(d, 3)
+    plan = xattn.get_plan(d.dims, 2)
+    if li in LONG_TAIL:
+        assert plan["unshared_splits"] > 0 and plan["partials"] > 0, plan
     g = xattn.StepGraph([dv.layer_step(d, o, lse, ws, nb, table_in, table_out, t_last)])
     try:
         g.launch()
