@@ -507,8 +507,12 @@ def measure(cfg, args, *, paged_rounds):
         achieved = alg["mfma_flops"] / call_s / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=peak_tflops, unit="TFLOP/s",
                     frac=round(achieved / peak_tflops, 4), traffic=measured_traffic(cfg))
+    folded_prompt = appends and s.plan["mfma"] == 1 and s.plan["partials"] > 0 and s.plan["unshared_splits"] > 0
     if fused:
         roof["kernel"] = "xattn_append_decode call (1 kernel launch: the append folded into the decode)"
+    elif folded_prompt:
+        roof["kernel"] = ("xattn_append_decode call (3 kernel launches: the prompt pass with the append folded "
+                          "in, the Non-Shared pass, the Merge)")
     elif appends:
         roof["kernel"] = "xattn_append_decode call (append, then %d decode launch%s)" % (
             s.plan["launches"], "" if s.plan["launches"] == 1 else "es")

@@ -234,6 +234,16 @@ bool append_folds(const xattn_dims* d, const Plan& p) {
          d->num_kv_heads <= kMaxAppendBlocks;
 }
 
+// With long generated tails (a Non-Shared pass of its own) the append folds
+// into the MFMA prompt pass instead, done by prompt split 0's workgroups: the
+// prompt pass reads neither the pool nor the tables, and the Non-Shared pass
+// launched after it finds them updated. Its arrival counters are the head of
+// the decode's counter block.
+bool append_folds_prompt_pass(const xattn_dims* d, const Plan& p) {
+  return p.mfma && p.parts > 0 && p.u_splits > 0 && !uses_fixup(d, p, 2) &&
+         d->max_unshared_len < (1 << kArrivalShift) && d->num_kv_heads <= kMaxAppendBlocks;
+}
+
 // which = 3 (xattn_append_decode): the arrival counters of a folded append,
 // else the decode's workspace.
 Layout layout_for(const xattn_dims* d, const Plan& p, int which) {
@@ -595,6 +605,18 @@ xattn_status xattn_append_decode(const xattn_dims* d, const void* q, const void*
   const size_t need = ws_bytes_for(d, p, 3);
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return XATTN_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (append_folds_prompt_pass(d, p)) {
+    if (d->num_requests == 0) return XATTN_OK;
+    const int64_t rows = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
+    const Workspace w = carve(d, p, 2, ws);
+    const FusedAppend fa{k_new, v_new, parent, slot_base, active, kp, vp, table_out, ulen};
+    if (run_prefix(d, p, kModePartial, q, ks, vs, poff, plen, nullptr, nullptr, table_in, ulen,
+                   OutSpec{o, lse, 0, 0}, w, st, &fa) != hipSuccess)
+      return XATTN_ERR_HIP;
+    if (run_gen(d, p, q, kp, vp, table_out, ulen, OutSpec{w.o, w.lse, rows, p.p_splits}, st) != hipSuccess)
+      return XATTN_ERR_HIP;
+    return hip_status(launch_merge_parts(rows, d->head_dim, p.parts, w.o, w.lse, o, lse, st));
+  }
   if (!append_folds(d, p)) {
     e = xattn_cache_append(d, k_new, v_new, parent, slot_base, active, kp, vp, table_in, table_out,
                            ulen, stream);

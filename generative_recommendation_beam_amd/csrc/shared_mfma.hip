@@ -695,7 +695,9 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   // the one before it, the scalar cache returning out of order.
   // Rows past the last query row compute on a copy of that row (their
   // columns of S^T and O^T are independent of the others) and store nothing.
-  const bool app = a.append != 0;  // fused append (uniform)
+  // Fused append (uniform): done by prompt split 0's workgroups (the only
+  // member without a prompt split).
+  const bool app = a.append != 0 && member == 0;
   const int row = tile * (RG * 32) + rg * 32 + ql;
   const bool row_ok = row < M;
   const int rowc = min(row, M - 1);
@@ -725,7 +727,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   // where the paths join): without Non-Shared tokens the reads go to
   // prefix_len[0], which always exists; slot cells are clamped to the row
   // and ignored beyond the length.
-  const int32_t* lenp = do_ns ? a.unshared_len + r : a.prefix_len;
+  const int32_t* lenp = (do_ns || app) ? a.unshared_len + r : a.prefix_len;
   const int32_t* trow = early_slots ? a.slot_table + ((int64_t)r * s.B + bq) * s.T_max : a.prefix_len;
   const int tlast = early_slots ? s.T_max - 1 : 0;
   const int lenv = lenp[zv];
@@ -858,9 +860,10 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
     }
   }
 
-  // Fused append. This workgroup owns the beams whose first query row is in
-  // its row tile: it copies their new K/V rows (head h) to the pool and, at
-  // head 0, writes their table_out rows. t comes from the length read above
+  // Fused append (prompt split 0's workgroups). This workgroup owns the
+  // beams whose first query row is in its row tile: it copies their new K/V
+  // rows (head h) to the pool and writes its kv head's share of their
+  // table_out rows. t comes from the length read above
   // (its low bits: other workgroups' arrivals only touch the bits from
   // kArrivalShift up); the workgroup arrives after its prompt loop (where
   // the workgroups of a request arrive spread out in time: same-address
@@ -876,13 +879,15 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   bool grow = false;
   int old_arr = 0;  // this workgroup's arrival (thread 0)
   uint4 cpv = make_uint4(0, 0, 0, 0);  // this thread's first K/V chunk to copy
-  if (app) {  // uniform; always member 0 with Non-Shared tokens
+  if (app) {  // uniform
     if (kg == 0 && row_ok && gq == 0) s_par[bq - b_lo] = parv;  // read after the next barrier
     t_app = __builtin_amdgcn_readfirstlane(lenv) & ((1 << kArrivalShift) - 1);
     grow = __builtin_amdgcn_readfirstlane(actv) != 0 && t_app < s.T_max;
-    ns.L = grow ? t_app + 1 : t_app;
-    ns.tnew = grow ? t_app : -1;
-    ns.trow = a.slot_table + ((int64_t)r * s.B + (grow ? parv : bq)) * s.T_max;
+    if (do_ns) {  // the beam's tokens in this pass: through the parent's row, the new one from k_new/v_new
+      ns.L = grow ? t_app + 1 : t_app;
+      ns.tnew = grow ? t_app : -1;
+      ns.trow = a.slot_table + ((int64_t)r * s.B + (grow ? parv : bq)) * s.T_max;
+    }
     // The first pass of the K/V copy: its source does not depend on t, so it
     // is requested now and stored right after the prompt loop.
     if (grow && tid < nb_own * 2 * (D / 8)) {
@@ -891,8 +896,10 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
                                             (((int64_t)r * s.B + b_lo + bl) * s.Hkv + h) * D + 8 * (pc % (D / 8)));
     }
     if constexpr (!PIPE) set_row_ptrs();
+    if (do_ns) {
 #pragma unroll
-    for (int u = 0; u < NSL; ++u) pslot[u] = ns.slot(u);
+      for (int u = 0; u < NSL; ++u) pslot[u] = ns.slot(u);
+    }
   }
   // Token block: every group holds at most one token (L <= 3); group kg < 3
   // moves token min(kg, L - 1) (a repeat is masked out), from the pool
@@ -1151,7 +1158,11 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   constexpr int CH = D / 8;                      // 16-byte chunks per K (or V) row
   const int n_cp = grow ? nb_own * 2 * CH : 0;   // K/V chunks to copy
   const int tc = grow ? t_app + 1 : t_app;       // table cells per owned row
-  const int n_tb = (app && h == 0) ? nb_own * tc : 0;
+  // The kv heads' workgroups share the owned rows' cells: head h copies
+  // columns [tj0, tj0 + tcw) (long rows are then no single workgroup's tail).
+  const int tj0 = (int)((int64_t)h * tc / s.Hkv);
+  const int tcw = (int)((int64_t)(h + 1) * tc / s.Hkv) - tj0;
+  const int n_tb = app ? nb_own * tcw : 0;
   const int64_t sb_new = sbv + (int64_t)t_app * s.B;  // slot of beam 0's new row
   auto cp_src = [&](int i) {
     const int bl = i / (2 * CH), pc = i - bl * (2 * CH);
@@ -1163,14 +1174,14 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
     uint16_t* base = pc < CH ? a.k_pool_out : a.v_pool_out;
     return reinterpret_cast<uint4*>(base + ((sb_new + b_lo + bl) * s.Hkv + h) * D + 8 * (pc % CH));
   };
-  auto tb_val = [&](int i) {  // table_out cell i of the owned rows
-    const int bl = i / tc, j = i - bl * tc;
+  auto tb_val = [&](int i) {  // table_out cell i of this head's share of the owned rows
+    const int bl = i / tcw, j = tj0 + (i - bl * tcw);
     if (j == t_app) return (int32_t)(sb_new + b_lo + bl);
     const int src = grow ? s_par[bl] : b_lo + bl;
     return a.slot_table[((int64_t)r * s.B + src) * s.T_max + j];
   };
   auto tb_dst = [&](int i) {
-    const int bl = i / tc, j = i - bl * tc;
+    const int bl = i / tcw, j = tj0 + (i - bl * tcw);
     return a.table_out + ((int64_t)r * s.B + b_lo + bl) * s.T_max + j;
   };
   int32_t tbv = 0;
@@ -1214,7 +1225,14 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   if (app) {  // uniform
     if (tid < n_tb) *tb_dst(tid) = tbv;
     for (int i = tid + NTH; i < n_cp; i += NTH) *cp_dst(i) = *cp_src(i);
-    for (int i = tid + NTH; i < n_tb; i += NTH) *tb_dst(i) = tb_val(i);
+    for (int i0 = tid + NTH; i0 < n_tb; i0 += 4 * NTH) {  // four cells in flight per thread
+      int32_t v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = i0 + k * NTH < n_tb ? tb_val(i0 + k * NTH) : 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (i0 + k * NTH < n_tb) *tb_dst(i0 + k * NTH) = v[k];
+    }
     if (tid == 0 && old_arr >= 0 && (old_arr >> kArrivalShift) == a.arrivals - 1)
       a.ulen_rw[r] = grow ? t_app + 1 : t_app;
   }

@@ -59,6 +59,14 @@ CASES = {
                   {}, False),
     "fallback_long": (dict(R=2, B=4, Hq=8, Hkv=2, D=128, prefix_len=[300, 100], unshared_len=[40, 25]), ONE,
                       False),
+    # long generated tails: the append folds into the prompt pass (split 0's
+    # workgroups), then the Non-Shared pass and the Merge
+    "long_splits": (dict(R=2, B=4, Hq=8, Hkv=2, D=128, prefix_len=[1500, 600], unshared_len=[40, 20]),
+                    dict(prefix_splits=3), False),
+    "long_full_rows": (dict(R=2, B=4, Hq=8, Hkv=2, D=128, prefix_len=[150, 260], unshared_len=[20, 18],
+                            T_max=20), ONE, False),
+    "long_no_prompt": (dict(R=2, B=3, Hq=4, Hkv=1, D=64, prefix_len=[0, 130], unshared_len=[30, 25]), ONE,
+                       False),
     "fallback_splits": (dict(R=2, B=12, Hq=8, Hkv=2, D=128, prefix_len=[640, 200], unshared_len=[3, 2]),
                         dict(prefix_splits=3), False),
     "fallback_f32": (dict(R=2, B=4, Hq=4, Hkv=1, D=64, prefix_len=[256, 100], unshared_len=[2, 3],
