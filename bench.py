@@ -511,8 +511,10 @@ def measure(cfg, args, *, paged_rounds):
     if fused:
         roof["kernel"] = "xattn_append_decode call (1 kernel launch: the append folded into the decode)"
     elif folded_prompt:
-        roof["kernel"] = ("xattn_append_decode call (3 kernel launches: the prompt pass with the append folded "
-                          "in, the Non-Shared pass, the Merge)")
+        roof["kernel"] = ("xattn_append_decode call (%d kernel launches: the prompt pass with the append folded "
+                          "in, then the Non-Shared pass%s)" % (
+                              s.plan["launches"], " folding the prompt's partials in" if s.plan["launches"] == 2
+                              else ", then the Merge"))
     elif appends:
         roof["kernel"] = "xattn_append_decode call (append, then %d decode launch%s)" % (
             s.plan["launches"], "" if s.plan["launches"] == 1 else "es")

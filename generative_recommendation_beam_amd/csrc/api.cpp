@@ -221,9 +221,14 @@ bool uses_fixup(const xattn_dims* d, const Plan& p, int which) {
 }
 
 // Kernel launches one call makes under plan p.
+// A decode's separate Non-Shared pass folds the prompt pass's partials into
+// the final outputs (its splits merged in one workgroup): no Merge launch.
+bool gen_folds_prompt(const Plan& p) { return p.u_splits > 0 && p.u_splits <= kValuWgMaxSplits; }
+
 int launches(const xattn_dims* d, const Plan& p, int which) {
   if (p.parts == 0 || uses_fixup(d, p, which)) return 1;
-  return 2 + ((which == 2 && p.u_splits > 0) ? 1 : 0);
+  if (which == 2 && p.u_splits > 0) return gen_folds_prompt(p) ? 2 : 3;
+  return 2;
 }
 
 // Does xattn_append_decode fold the append into a single decode launch
@@ -367,7 +372,7 @@ hipError_t run_prefix(const xattn_dims* d, const Plan& p, int mode, const void* 
     }
     return launch_shared_mfma(a, st);
   }
-  ValuArgs a;
+  ValuArgs a{};
   a.s = make_shape(d);
   a.dtype = d->dtype;
   a.q = q;
@@ -387,10 +392,12 @@ hipError_t run_prefix(const xattn_dims* d, const Plan& p, int mode, const void* 
   return launch_valu_attn(a, st);
 }
 
+// fold: the prompt pass's partial slots (workspace) folded into final
+// outputs by this launch (no Merge launch); null: `out` as given.
 hipError_t run_gen(const xattn_dims* d, const Plan& p, const void* q, const void* kp,
                    const void* vp, const int32_t* table, const int32_t* ulen, OutSpec out,
-                   hipStream_t st) {
-  ValuArgs a;
+                   hipStream_t st, const Workspace* fold = nullptr) {
+  ValuArgs a{};
   a.s = make_shape(d);
   a.dtype = d->dtype;
   a.q = q;
@@ -407,8 +414,16 @@ hipError_t run_gen(const xattn_dims* d, const Plan& p, const void* q, const void
   a.splits = std::max(1, p.u_splits);
   a.chunk = p.u_chunk;
   a.out = out;
+  if (fold) {
+    a.fold_o = fold->o;
+    a.fold_lse = fold->lse;
+    a.fold_parts = p.p_splits;
+    a.fold_stride = (int64_t)d->num_requests * d->beam_width * d->num_q_heads;
+  }
   return launch_valu_attn(a, st);
 }
+
+
 
 }  // namespace
 
@@ -543,6 +558,8 @@ xattn_status xattn_decode(const xattn_dims* d, const void* q, const void* ks, co
                              fused ? vp : nullptr, table, ulen, fin, w, st);
   if (he != hipSuccess) return XATTN_ERR_HIP;
   if (!fused) {
+    if (gen_folds_prompt(p))  // the Non-Shared pass merges everything into o/lse
+      return hip_status(run_gen(d, p, q, kp, vp, table, ulen, fin, st, &w));
     he = run_gen(d, p, q, kp, vp, table, ulen, OutSpec{w.o, w.lse, rows, p.p_splits}, st);
     if (he != hipSuccess) return XATTN_ERR_HIP;
   }
@@ -613,6 +630,8 @@ xattn_status xattn_append_decode(const xattn_dims* d, const void* q, const void*
     if (run_prefix(d, p, kModePartial, q, ks, vs, poff, plen, nullptr, nullptr, table_in, ulen,
                    OutSpec{o, lse, 0, 0}, w, st, &fa) != hipSuccess)
       return XATTN_ERR_HIP;
+    if (gen_folds_prompt(p))  // the Non-Shared pass merges everything into o/lse
+      return hip_status(run_gen(d, p, q, kp, vp, table_out, ulen, OutSpec{o, lse, 0, 0}, st, &w));
     if (run_gen(d, p, q, kp, vp, table_out, ulen, OutSpec{w.o, w.lse, rows, p.p_splits}, st) != hipSuccess)
       return XATTN_ERR_HIP;
     return hip_status(launch_merge_parts(rows, d->head_dim, p.parts, w.o, w.lse, o, lse, st));

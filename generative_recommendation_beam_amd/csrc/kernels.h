@@ -97,7 +97,16 @@ struct ValuArgs {
   int splits;       // key-range splits (over the prompt if use_prefix, else over generated)
   int chunk;        // keys per split
   OutSpec out;      // writes slot part_base + split when out.part_stride != 0
+  // Partials folded into the final output by the LSE rule (the prompt
+  // splits an earlier launch wrote): fold_parts slots of [fold_stride][D]
+  // and [fold_stride]; 0 = none. Needs final outputs, and splits merged in
+  // one workgroup (splits <= kValuWgMaxSplits).
+  const float* fold_o;
+  const float* fold_lse;
+  int fold_parts;
+  int64_t fold_stride;
 };
+constexpr int kValuWgMaxSplits = 8;  // splits merged inside one workgroup (one wave each), at most
 hipError_t launch_valu_attn(const ValuArgs& a, hipStream_t st);
 
 // ---- Merge (merge.hip) ----

@@ -25,7 +25,8 @@ namespace xattn {
 namespace {
 
 constexpr int kValuWaves = 4;
-constexpr int kValuWgMax = 8;  // splits merged inside one workgroup (one wave each), at most
+constexpr int kValuWgMax = kValuWgMaxSplits;
+constexpr int kValuFoldChunk = 4;  // folded partials whose loads are in flight together
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -288,6 +289,8 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
     }
   }
   st.combine_slots(lane);
+  // The wave (split) that finalizes query head g of the group.
+  auto owner = [&](int g) { return (WGM && a.fold_parts > 0) ? g % a.splits : 0; };
 
   if constexpr (WGM) {  // the grid holds exactly n_units waves: all reach the barrier
     __shared__ float s_ml[kValuWgMax][NG][2];
@@ -304,9 +307,11 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
       }
     }
     __syncthreads();
-    if (split != 0) return;  // uniform per wavefront
+    // Wave w finalizes the query heads g with g % splits == w (without a
+    // fold, wave 0 takes them all: the order of the writes does not matter).
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
+      if (owner(g) != split) continue;  // uniform per wavefront
       float mt = neg_inf();
       for (int w = 0; w < a.splits; ++w) mt = fmaxf(mt, s_ml[w][g][0]);
       float lt = 0.f;
@@ -325,6 +330,52 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
   }
   if (slot_id != 0) return;
   const int64_t row0 = n * s.Hq + h * G + g0;
+  if (a.fold_parts > 0) {
+    // Fold the earlier launch's partials (normalized O, natural-log lse) into
+    // this state: a partial weighs 2^(lse*log2(e) - m) against the new offset
+    // m. kValuFoldChunk partials' loads are in flight together.
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (g >= ng) break;
+      if (owner(g) != split) continue;  // uniform per wavefront
+      const int64_t row = row0 + g;
+      for (int p0 = 0; p0 < a.fold_parts; p0 += kValuFoldChunk) {
+        float lp[kValuFoldChunk];
+        float4 ov[kValuFoldChunk][EPL / 4];
+#pragma unroll
+        for (int q = 0; q < kValuFoldChunk; ++q) {
+          const int p = min(p0 + q, a.fold_parts - 1);  // past the last: a repeat, weight 0 below
+          lp[q] = a.fold_lse[p * a.fold_stride + row] * kLog2e;
+          const float* po = a.fold_o + (p * a.fold_stride + row) * D + dl * EPL;
+#pragma unroll
+          for (int e = 0; e < EPL / 4; ++e) ov[q][e] = *reinterpret_cast<const float4*>(po + 4 * e);
+        }
+        float mt = st.m[g];
+#pragma unroll
+        for (int q = 0; q < kValuFoldChunk; ++q)
+          if (p0 + q < a.fold_parts) mt = fmaxf(mt, lp[q]);
+        const float sc = (mt == neg_inf() || st.m[g] == neg_inf()) ? 0.f : exp2_approx(st.m[g] - mt);
+        float lt = st.l[g] * sc;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) st.acc[g][e] *= sc;
+#pragma unroll
+        for (int q = 0; q < kValuFoldChunk; ++q) {
+          const float wgt =
+              (p0 + q >= a.fold_parts || mt == neg_inf() || lp[q] == neg_inf()) ? 0.f : exp2_approx(lp[q] - mt);
+          lt += wgt;
+#pragma unroll
+          for (int e = 0; e < EPL / 4; ++e) {
+            st.acc[g][4 * e] += ov[q][e].x * wgt;
+            st.acc[g][4 * e + 1] += ov[q][e].y * wgt;
+            st.acc[g][4 * e + 2] += ov[q][e].z * wgt;
+            st.acc[g][4 * e + 3] += ov[q][e].w * wgt;
+          }
+        }
+        st.m[g] = mt;
+        st.l[g] = lt;
+      }
+    }
+  }
   float* ob = a.out.o;
   float* lb = a.out.lse;
   if (a.out.part_stride) {
@@ -335,6 +386,7 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     if (g >= ng) break;
+    if (owner(g) != (WGM ? split : 0)) continue;  // uniform per wavefront
     const float l = st.l[g];
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     float* dst = ob + (row0 + g) * D + dl * EPL;

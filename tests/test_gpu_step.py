@@ -25,8 +25,8 @@ LAYERS = [
     dict(R=3, B=8, Hq=4, Hkv=1, D=64, prefix_len=[130, 0, 64], unshared_len=[2, 1, 3]),
     dict(R=2, B=40, Hq=16, Hkv=4, D=128, prefix_len=[700, 1100], unshared_len=[1, 4]),
     dict(R=1, B=4, Hq=4, Hkv=1, D=64, prefix_len=[256], unshared_len=[2], dtype="f32"),
-    # long generated tails: the prompt pass, a Non-Shared pass of its own and
-    # the Merge, all captured
+    # long generated tails: the prompt pass (with the append), then a
+    # Non-Shared pass of its own that folds the prompt's partials in
     dict(R=2, B=4, Hq=8, Hkv=2, D=128, prefix_len=[600, 300], unshared_len=[40, 20]),
     dict(R=2, B=3, Hq=4, Hkv=1, D=64, prefix_len=[0, 150], unshared_len=[30, 25]),
 ]
@@ -97,7 +97,8 @@ def test_step_graph_every_replay_matches_oracle():
 @pytest.mark.parametrize("li", [0] + LONG_TAIL)
 def test_step_graph_equals_eager_bitwise(li):
     """A replay gives the same bits as the eager calls it captured (for the
-    long tails: three launches per layer)."""
+    long tails: the prompt pass with the append, then the Non-Shared pass
+    that merges everything)."""
     kw = LAYERS[li]
     w = make_workload("stepE", seed_key=(321, li), **kw)
     d = dv.upload(w)
