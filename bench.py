@@ -101,6 +101,9 @@ def append_bytes(w):
 
 
 KERNEL_SOURCES = ("generative_recommendation_beam_amd/csrc/shared_mfma.hip",
+                  "generative_recommendation_beam_amd/csrc/valu_attn.hip",
+                  "generative_recommendation_beam_amd/csrc/append.hip",
+                  "generative_recommendation_beam_amd/csrc/merge.hip",
                   "generative_recommendation_beam_amd/csrc/device.h",
                   "generative_recommendation_beam_amd/csrc/kernels.h",
                   "generative_recommendation_beam_amd/csrc/api.cpp")
@@ -280,10 +283,12 @@ def time_graph(g, K, before=None):
 
 
 def time_parts(s, K):
-    """The same layers through the separate calls, eager, HIP events around
-    each: the unfused path (Shared stage, Non-Shared stage, Merge) on the
-    complete caches, and the append alone (lengths restored before each
-    round, outside the events)."""
+    """The same layers through the separate calls. Each kind of call is
+    captured as one graph of the n_layers calls (torch's graph capture of the
+    library's launches on the capture stream) and timed like the fused call,
+    K launches between HIP events, interval / n_layers: the unfused path
+    (Shared stage, Non-Shared stage, Merge) on the complete caches, and the
+    append alone (lengths restored before each launch, outside the events)."""
     import numpy as np
     import torch
     from generative_recommendation_beam_amd import xattn
@@ -299,48 +304,54 @@ def time_parts(s, K):
                          w0=torch.zeros(max(n0, 1), dtype=torch.uint8, device="cuda"), n0=n0,
                          w1=torch.zeros(max(n1, 1), dtype=torch.uint8, device="cuda"), n1=n1,
                          tscratch=torch.empty_like(tout)))
+    layers = list(zip(s.layers, bufs))
 
-    def unfused(evs):
-        for (d, o, lse, ws, nb, tin, tout, t_last), b, e in zip(s.layers, bufs, evs):
-            e[0].record()
+    def shared():
+        for (d, o, lse, ws, nb, tin, tout, t_last), b in layers:
             xattn.shared_stage(d.dims, d.q, d.k_shared, d.v_shared, d.prefix_off, d.prefix_len, b["os"], b["ls"],
                                b["w0"] if b["n0"] else None, b["n0"])
-            e[1].record()
+
+    def unshared():
+        for (d, o, lse, ws, nb, tin, tout, t_last), b in layers:
             xattn.unshared_stage(d.dims, d.q, d.k_pool, d.v_pool, tout, d.unshared_len, b["ou"], b["lu"],
                                  b["w1"] if b["n1"] else None, b["n1"])
-            e[2].record()
-            xattn.merge(d.rows, d.w.D, b["os"], b["ls"], b["ou"], b["lu"], o, lse)
-            e[3].record()
 
-    def appends(evs):
-        s.ulen_all.copy_(s.ulen0)
-        for (d, o, lse, ws, nb, tin, tout, t_last), b, e in zip(s.layers, bufs, evs):
-            e[0].record()
+    def merge():
+        for (d, o, lse, ws, nb, tin, tout, t_last), b in layers:
+            xattn.merge(d.rows, d.w.D, b["os"], b["ls"], b["ou"], b["lu"], o, lse)
+
+    def appends():
+        for (d, o, lse, ws, nb, tin, tout, t_last), b in layers:
             xattn.cache_append(d.dims, d.k_new[t_last], d.v_new[t_last], s.sel_parent, d.slot_base,
                                d.active[t_last], d.k_pool, d.v_pool, tin, b["tscratch"], d.unshared_len)
-            e[1].record()
 
+    class _Replay:
+        def __init__(self, fn):
+            fn()  # eager warm-up
+            torch.cuda.synchronize()
+            self.g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(self.g):
+                fn()
+            torch.cuda.synchronize()
+
+        def launch(self):
+            self.g.replay()
+
+    n = len(s.layers)
+    per_call = lambda ms: round(float(np.median(ms)) * 1e3 / n, 3)
     # complete caches: lengths as after the step
     s.one_step()
     torch.cuda.synchronize()
-    unfused([[_ev() for _ in range(4)] for _ in s.layers])  # warm-up
-    rounds = [[[_ev() for _ in range(4)] for _ in s.layers] for _ in range(K)]
-    for r in rounds:
-        unfused(r)
-    torch.cuda.synchronize()
-    sh = np.array([[e[0].elapsed_time(e[1]) for e in r] for r in rounds]) * 1e3
-    un = np.array([[e[1].elapsed_time(e[2]) for e in r] for r in rounds]) * 1e3
-    mg = np.array([[e[2].elapsed_time(e[3]) for e in r] for r in rounds]) * 1e3
-    out = dict(shared_us=round(float(np.median(sh)), 3), unshared_us=round(float(np.median(un)), 3),
-               merge_us=round(float(np.median(mg)), 3))
+    out = dict(shared_us=per_call(time_graph(_Replay(shared), K)),
+               unshared_us=per_call(time_graph(_Replay(unshared), K)),
+               merge_us=per_call(time_graph(_Replay(merge), K)))
     out["unfused_us"] = round(out["shared_us"] + out["unshared_us"] + out["merge_us"], 3)
     if s.layers[0][7] is not None:
-        appends([[_ev(), _ev()] for _ in s.layers])
-        ar = [[[_ev(), _ev()] for _ in s.layers] for _ in range(K)]
-        for r in ar:
-            appends(r)
-        torch.cuda.synchronize()
-        out["append_us"] = round(float(np.median([[e[0].elapsed_time(e[1]) for e in r] for r in ar])) * 1e3, 3)
+        restore = lambda: s.ulen_all.copy_(s.ulen0)
+        restore()
+        g = _Replay(appends)
+        out["append_us"] = per_call(time_graph(g, K, restore))
+    out["timing"] = "each kind of call captured as one graph of the n_layers calls, K launches, interval / n_layers"
     # leave the caches as a step leaves them
     s.one_step()
     torch.cuda.synchronize()
