@@ -153,7 +153,8 @@ class Setup:
         self.ulen_all = torch.zeros((n_layers, max(w0.R, 1)), dtype=torch.int32, device="cuda")
         self.layers = []
         for l, w in enumerate(self.layers_np):
-            d = dv.upload(w, prefix_splits=args.prefix_splits, rows_per_block=args.rows_per_block,
+            d = dv.upload(w, prefix_splits=args.prefix_splits, unshared_splits=args.unshared_splits,
+                          rows_per_block=args.rows_per_block,
                           pipeline_stages=args.stages, key_groups=args.key_groups)
             d.unshared_len = self.ulen_all[l]
             table_in, table_out, t_last = dv.prepare_step(d)
@@ -596,6 +597,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--prefix-splits", type=int, default=0, help="override the split plan (0 = auto)")
+    ap.add_argument("--unshared-splits", type=int, default=0,
+                    help="override the generated-token splits (0 = auto)")
     ap.add_argument("--rows-per-block", type=int, default=0, help="override rows per workgroup (0 = auto)")
     ap.add_argument("--stages", type=int, default=0, help="override LDS pipeline stages (0 = auto)")
     ap.add_argument("--key-groups", type=int, default=0, help="override key groups per workgroup (0 = auto)")

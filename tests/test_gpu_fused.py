@@ -67,6 +67,14 @@ CASES = {
                             T_max=20), ONE, False),
     "long_no_prompt": (dict(R=2, B=3, Hq=4, Hkv=1, D=64, prefix_len=[0, 130], unshared_len=[30, 25]), ONE,
                        False),
+    # the Non-Shared pass's splits as the waves of one workgroup folding the
+    # prompt partials in: more query heads than splits, fewer, and eight
+    "long_fold_3splits": (dict(R=2, B=3, Hq=8, Hkv=2, D=128, prefix_len=[900, 200], unshared_len=[70, 41]),
+                          dict(unshared_splits=3), False),
+    "long_fold_8splits_g8": (dict(R=1, B=4, Hq=16, Hkv=2, D=128, prefix_len=[700], unshared_len=[90]),
+                             dict(unshared_splits=8, prefix_splits=2), False),
+    "long_fold_2splits_d64": (dict(R=2, B=2, Hq=4, Hkv=1, D=64, prefix_len=[300, 0], unshared_len=[33, 20]),
+                              dict(unshared_splits=2), False),
     "fallback_splits": (dict(R=2, B=12, Hq=8, Hkv=2, D=128, prefix_len=[640, 200], unshared_len=[3, 2]),
                         dict(prefix_splits=3), False),
     "fallback_f32": (dict(R=2, B=4, Hq=4, Hkv=1, D=64, prefix_len=[256, 100], unshared_len=[2, 3],
