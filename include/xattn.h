@@ -177,8 +177,11 @@ xattn_status xattn_merge(int64_t rows, int32_t head_dim, const float* o_a, const
  * Fused decode attention: Shared stage + Non-Shared stage + Merge in one pass
  * (the measured call). The Non-Shared part runs in the Shared stage's
  * epilogue when the plan fuses it; otherwise it runs as its own split work
- * and one reduction merges all partials. Writes o [N_b][H_q][D] and, if lse
- * is not NULL, lse [N_b][H_q].
+ * and the partials are combined by the log-sum-exp rule: when the plan gives
+ * the Non-Shared tokens a vector pass of their own with at most 8 splits
+ * (long generated tails), that pass folds the prompt partials in and writes
+ * o and lse itself; in every other split plan one reduction merges all
+ * partials. Writes o [N_b][H_q][D] and, if lse is not NULL, lse [N_b][H_q].
  */
 xattn_status xattn_decode(const xattn_dims* dims, const void* q, const void* k_shared,
                           const void* v_shared, const int64_t* prefix_off,
@@ -234,9 +237,15 @@ xattn_status xattn_cache_append(const xattn_dims* dims, const void* k_new, const
  * its new token straight from k_new / v_new, and writes the pool rows,
  * table_out rows and lengths of the beams it owns; arrivals are counted per
  * (request, kv head) in the workspace (which = 3 in xattn_workspace_size),
- * then per request on unshared_len. Otherwise the two calls are made in
- * order, with the decode's workspace. Same limits and errors as the two
- * calls, and XATTN_ERR_INVALID_ARG if table_out == table_in.
+ * then per request on unshared_len. When the plan gives the Non-Shared
+ * tokens a vector pass of their own (long generated tails, bf16) the append
+ * folds into the MFMA prompt pass instead: prompt split 0's workgroups write
+ * the pool rows, table_out rows and lengths (the prompt pass reads neither
+ * the pool nor the tables), the Non-Shared pass after it reads table_out, and
+ * its arrival counters are the head of the decode's workspace. Otherwise the
+ * two calls are made in order, with the decode's workspace. Same limits and
+ * errors as the two calls, and XATTN_ERR_INVALID_ARG if table_out ==
+ * table_in.
  */
 xattn_status xattn_append_decode(const xattn_dims* dims, const void* q, const void* k_shared,
                                  const void* v_shared, const int64_t* prefix_off,
