@@ -142,7 +142,24 @@ struct LoadPlan {
 
 typedef __attribute__((address_space(3))) char lds_char;
 
-__device__ __forceinline__ void wait_vmem() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// vmcnt(n) as an s_waitcnt immediate (vmcnt in bits 3:0 and 15:14; expcnt
+// in 6:4 and lgkmcnt in 11:8 left at their maxima, i.e. not waited for).
+constexpr int vm_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+
+// Wait until at most N vector-memory operations are in flight. Through the
+// builtin rather than inline assembly, so that the compiler's own wait
+// insertion sees it: the loads it issued earlier (query rows, per-request
+// values) then count as landed there, and it adds no waits of its own for
+// them behind the direct-to-LDS loads that follow (which it does not track).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt field");
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(vm_imm(N));
+  __asm__ volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void wait_vmem() { wait_vm<0>(); }
 
 // Split partials that one workgroup hands to another are written and read
 // with agent-coherent buffer accesses (cache policy sc1, what agent-scope
@@ -190,14 +207,12 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 // Online-softmax update for one 32-key half of a tile (S^T block `sb`, the
-// 16 scores this lane holds for its query column), followed by that half's
-// P.V MFMAs. Processing the halves separately lets the vector-ALU softmax of
-// one half overlap the matrix-core work of the other.
-template <int D, bool MASK, bool NO_HI1 = false>
-__device__ __forceinline__ void half_softmax_pv(const char* buf, int vbase, f32x16_t& sb, int kb,
-                                                f32x16_t* oacc, float& m_run, float& l_part, float c,
-                                                int hh, int nvalid) {
-  using TG = TileGeom<D>;
+// 16 scores this lane holds for its query column): the offset moves (and the
+// output so far is rescaled) when a score passes it, and the half's
+// probabilities are packed to bf16 in pf for its P.V MFMAs.
+template <int D, bool MASK>
+__device__ __forceinline__ void half_softmax(f32x16_t& sb, int kb, f32x16_t* oacc, float& m_run, float& l_part,
+                                             float c, int hh, int nvalid, bf16x8_t* pf) {
   constexpr int NDB = D / 32;
   if (MASK) {
 #pragma unroll
@@ -221,7 +236,6 @@ __device__ __forceinline__ void half_softmax_pv(const char* buf, int vbase, f32x
     l_part *= alpha;
     m_run = mn;
   }
-  bf16x8_t pf[2];
   float lsum = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -230,6 +244,19 @@ __device__ __forceinline__ void half_softmax_pv(const char* buf, int vbase, f32x
     pf[i >> 3][i & 7] = (__bf16)p;
   }
   l_part += lsum;
+}
+
+// half_softmax followed by that half's P.V MFMAs. Processing the halves
+// separately lets the vector-ALU softmax of one half overlap the matrix-core
+// work of the other.
+template <int D, bool MASK, bool NO_HI1 = false>
+__device__ __forceinline__ void half_softmax_pv(const char* buf, int vbase, f32x16_t& sb, int kb,
+                                                f32x16_t* oacc, float& m_run, float& l_part, float c,
+                                                int hh, int nvalid) {
+  using TG = TileGeom<D>;
+  constexpr int NDB = D / 32;
+  bf16x8_t pf[2];
+  half_softmax<D, MASK>(sb, kb, oacc, m_run, l_part, c, hh, nvalid, pf);
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -487,15 +514,15 @@ __device__ __forceinline__ float pipe_pv_then_max(const char* buf, int vbase, in
 // field needs an immediate (at most 63), so n is rounded down to a multiple
 // of 8 (a smaller count only waits longer).
 __device__ __forceinline__ void wait_vm_at_most(int n) {
-  if (n >= 63) __asm__ volatile("s_waitcnt vmcnt(63)" ::: "memory");
-  else if (n >= 56) __asm__ volatile("s_waitcnt vmcnt(56)" ::: "memory");
-  else if (n >= 48) __asm__ volatile("s_waitcnt vmcnt(48)" ::: "memory");
-  else if (n >= 40) __asm__ volatile("s_waitcnt vmcnt(40)" ::: "memory");
-  else if (n >= 32) __asm__ volatile("s_waitcnt vmcnt(32)" ::: "memory");
-  else if (n >= 24) __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory");
-  else if (n >= 16) __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if (n >= 8) __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (n >= 63) wait_vm<63>();
+  else if (n >= 56) wait_vm<56>();
+  else if (n >= 48) wait_vm<48>();
+  else if (n >= 40) wait_vm<40>();
+  else if (n >= 32) wait_vm<32>();
+  else if (n >= 24) wait_vm<24>();
+  else if (n >= 16) wait_vm<16>();
+  else if (n >= 8) wait_vm<8>();
+  else wait_vm<0>();
 }
 
 // Wait until at most N (if keep) or no vector-memory operations are in
@@ -504,9 +531,9 @@ template <int N>
 __device__ __forceinline__ void wait_vm_keep(bool keep) {
   static_assert(N >= 0 && N <= 63, "vmcnt field");
   if (keep)
-    __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    wait_vm<N>();
   else
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vm<0>();
 }
 
 // Wait until at most `ahead` tiles' loads (each `lpt` instructions per wave)
@@ -517,9 +544,9 @@ __device__ __forceinline__ void wait_tiles(int ahead) {
   constexpr int one = LPT < 63 ? LPT : 63;
   constexpr int two = 2 * LPT < 63 ? 2 * LPT : 63;
   switch (ahead) {
-    case 0: __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(one) : "memory"); break;
-    default: __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(two) : "memory"); break;
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<one>(); break;
+    default: wait_vm<two>(); break;
   }
 }
 
@@ -779,8 +806,6 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   lp.init(wave, lane);
   lds_char* lsm = (lds_char*)smem;
   const int prompt_bytes = P * TG::ROWB;
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, (short)0, prompt_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, (short)0, prompt_bytes, 0x00020000);
   // Direct HBM->LDS loads of super-tile t into its stage buffer. Buffer loads
   // address the prompt through descriptors bounded to its P_r rows, so keys
   // past the prompt read as zero (they are masked) and no load leaves it; the
@@ -792,24 +817,28 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   // the workgroup that started there. The last (possibly partial) super-tile
   // stays last. The softmax result does not depend on the order.
   const int rot = (KG >= 2 && nsup > 2) ? tile % (nsup - 1) : 0;
+  // The loads go through lds_dma16 (the walks wait for them with explicit
+  // vmcnt counts and publish them with a barrier); the refill of the other
+  // stage is then no reason for the compiler to wait before this stage's
+  // LDS reads.
+  const i32x4_t rk_w = raw_rsrc_words(Kg, prompt_bytes);
+  const i32x4_t rv_w = raw_rsrc_words(Vg, prompt_bytes);
   auto issue_part = [&](int t, bool do_k, bool do_v) {
-    lds_char* buf = lsm + (t % NS) * SBUF + wave * 1024;
+    const uint32_t buf = (uint32_t)(uintptr_t)lsm + (uint32_t)((t % NS) * SBUF + wave * 1024);
     const int pt = t < nsup - 1 ? (t + rot) % (nsup - 1) : t;  // super-tile loaded at step t
     // (uniform: kept in a scalar register, the loads' scalar offset)
     const uint32_t tile_bytes = __builtin_amdgcn_readfirstlane((uint32_t)((kbeg + pt * ST) * TG::ROWB));
 #pragma unroll
-    for (int j = 0; j < LP::NJ; ++j) {
-      if (do_k) __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, buf + LP::lds_off(j), 16, lp.k[j], tile_bytes, 0, 0);
-      if (do_v)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, buf + LP::lds_off(j) + TG::TILEB, 16, lp.v[j], tile_bytes, 0, 0);
-    }
+    for (int j = 0; j < LP::NJ; ++j)
+      if (do_k) lds_dma16(rk_w, __builtin_amdgcn_readfirstlane(buf + LP::lds_off(j)), lp.k[j], tile_bytes);
+#pragma unroll
+    for (int j = 0; j < LP::NJ; ++j)
+      if (do_v) lds_dma16(rv_w, __builtin_amdgcn_readfirstlane(buf + LP::lds_off(j) + TG::TILEB), lp.v[j], tile_bytes);
   };
   auto issue_tile = [&](int t) { issue_part(t, true, true); };
-  // The pipelined walk refills the K and V halves of a stage separately and
-  // through lds_dma16 (all K loads of a tile, then all V loads, so that
-  // vmcnt counts them in that order).
-  const i32x4_t rk_w = raw_rsrc_words(Kg, prompt_bytes);
-  const i32x4_t rv_w = raw_rsrc_words(Vg, prompt_bytes);
+  // The pipelined walk refills the K and V halves of a stage separately (all
+  // K loads of a tile, then all V loads, so that vmcnt counts them in that
+  // order).
   auto issue_asm = [&](int t, bool is_v) {  // full tile t (no rotation with one key group)
     const uint32_t base = (uint32_t)(uintptr_t)lsm + (uint32_t)((t % NS) * SBUF + wave * 1024 + (is_v ? TG::TILEB : 0));
     const uint32_t tile_bytes = __builtin_amdgcn_readfirstlane((uint32_t)((kbeg + t * ST) * TG::ROWB));
@@ -988,11 +1017,11 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   int v_pending = -1;
   auto advance = [&](int it) {
     if (NPF > 0 && NS == 2 && it == 1)  // the token rows requested after tile 1's loads may stay in flight
-      __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(NPF * (NDC + 4 * NDB)) : "memory");
+      wait_vm<NPF * (NDC + 4 * NDB)>();
     else if (NPF > 0 && NS > 2)
       wait_vm_at_most(min(issued - 1 - it, NS - 2) * LPT + (tok_after >= it ? NPF * (NDC + 4 * NDB) : 0));
     else
-      wait_tiles<LPT>(min(issued - 1 - it, NS - 2));
+      wait_tiles<LPT>(NS == 2 ? 0 : min(issued - 1 - it, NS - 2));
     __syncthreads();  // super-tile `it` landed for every wave; it-1's buffer is free
     if (it == tok_at) issue_tok();  // before the refill: nothing is in flight here
     v_pending = -1;
@@ -1093,6 +1122,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
     }
     // Without two full tiles, or for the partial last tile: the masked step
     // (its loads requested now when the walk left them out).
+    if (!pipe) wait_vmem();  // (the walk waited already) the query rows have landed
     for (int it = pipe ? nfull : 0; it < nsup; ++it) {
       if (pipe && issued <= it) {
         issue_tile(it);
@@ -1111,6 +1141,10 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
       }
     }
   } else {
+  // The query rows (and the prologue's other register loads) have landed:
+  // with that wait visible to the compiler it puts none of its own inside
+  // the loop. (Two stages: the first step waits for everything anyway.)
+  wait_vmem();
   // This wave's tile of super-tile `it` sits at stage (it % NS), slot kg.
   for (int it = 0; it + 1 < nsup; ++it) {  // full super-tiles
     advance(it);
