@@ -379,7 +379,7 @@ def stream_bandwidth(nbytes=4 << 30, reps=10):
     med = statistics.median(ms)
     return dict(read_GBps=round(nbytes / (med * 1e-3) / 1e9, 1), bytes=nbytes, reps=reps,
                 frac_of_peak=round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                kernel="xattn_stream_read (16-byte loads, data discarded), median of the launches")
+                kernel="xattn_stream_read (16-byte non-temporal loads, data discarded), median of the launches")
 
 
 def cpu_baseline(cfg, seconds, single_core, single_seconds):

@@ -382,13 +382,26 @@ __device__ __forceinline__ i32x4_t raw_rsrc_words(const void* base, int num_reco
 // the lds bit) to LDS byte address `lds` (uniform), written as inline
 // assembly: the compiler's wait insertion cannot tell which LDS range such a
 // load writes and would wait for every one in flight before each LDS read
-// of the other stage. The pipelined walk waits for these loads itself
-// (vmcnt) and publishes them with a barrier. No register is written.
+// of the other stage. The walks wait for these loads themselves (vmcnt) and
+// publish them with a barrier. No register is written. NT marks the load
+// non-temporal (chosen per call, outside the unrolled load sequences). Measured on MI355X: for keys that no other
+// workgroup reads (a single row tile) streaming them is faster (64 distinct
+// 4608-token sequences, one decode: 226 -> 201 us); where the row tiles of
+// a (request, kv head) share the keys through L2 it is slower (16 requests
+// of 256 beams over 16384-token prompts: 2026 -> 2153 us), so those keep
+// the default policy.
+template <bool NT>
 __device__ __forceinline__ void lds_dma16(i32x4_t rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
-  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                   :
-                   : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-                   : "memory", "m0");
+  if constexpr (NT)
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                     :
+                     : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                     : "memory", "m0");
+  else
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :
+                     : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                     : "memory", "m0");
 }
 
 // ---- Software-pipelined walk over full 64-key tiles (one key group) ----
@@ -823,17 +836,26 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   // LDS reads.
   const i32x4_t rk_w = raw_rsrc_words(Kg, prompt_bytes);
   const i32x4_t rv_w = raw_rsrc_words(Vg, prompt_bytes);
+  const bool stream = a.row_tiles == 1;  // this workgroup is its keys' only reader
   auto issue_part = [&](int t, bool do_k, bool do_v) {
     const uint32_t buf = (uint32_t)(uintptr_t)lsm + (uint32_t)((t % NS) * SBUF + wave * 1024);
     const int pt = t < nsup - 1 ? (t + rot) % (nsup - 1) : t;  // super-tile loaded at step t
     // (uniform: kept in a scalar register, the loads' scalar offset)
     const uint32_t tile_bytes = __builtin_amdgcn_readfirstlane((uint32_t)((kbeg + pt * ST) * TG::ROWB));
+    auto go = [&](auto nt_c) {
+      constexpr bool NT = decltype(nt_c)::value;
 #pragma unroll
-    for (int j = 0; j < LP::NJ; ++j)
-      if (do_k) lds_dma16(rk_w, __builtin_amdgcn_readfirstlane(buf + LP::lds_off(j)), lp.k[j], tile_bytes);
+      for (int j = 0; j < LP::NJ; ++j)
+        if (do_k) lds_dma16<NT>(rk_w, __builtin_amdgcn_readfirstlane(buf + LP::lds_off(j)), lp.k[j], tile_bytes);
 #pragma unroll
-    for (int j = 0; j < LP::NJ; ++j)
-      if (do_v) lds_dma16(rv_w, __builtin_amdgcn_readfirstlane(buf + LP::lds_off(j) + TG::TILEB), lp.v[j], tile_bytes);
+      for (int j = 0; j < LP::NJ; ++j)
+        if (do_v)
+          lds_dma16<NT>(rv_w, __builtin_amdgcn_readfirstlane(buf + LP::lds_off(j) + TG::TILEB), lp.v[j], tile_bytes);
+    };
+    if (stream)
+      go(std::true_type{});
+    else
+      go(std::false_type{});
   };
   auto issue_tile = [&](int t) { issue_part(t, true, true); };
   // The pipelined walk refills the K and V halves of a stage separately (all
@@ -842,10 +864,17 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   auto issue_asm = [&](int t, bool is_v) {  // full tile t (no rotation with one key group)
     const uint32_t base = (uint32_t)(uintptr_t)lsm + (uint32_t)((t % NS) * SBUF + wave * 1024 + (is_v ? TG::TILEB : 0));
     const uint32_t tile_bytes = __builtin_amdgcn_readfirstlane((uint32_t)((kbeg + t * ST) * TG::ROWB));
+    auto go = [&](auto nt_c) {
+      constexpr bool NT = decltype(nt_c)::value;
 #pragma unroll
-    for (int j = 0; j < LP::NJ; ++j)
-      lds_dma16(is_v ? rv_w : rk_w, __builtin_amdgcn_readfirstlane(base + LP::lds_off(j)), is_v ? lp.v[j] : lp.k[j],
-                tile_bytes);
+      for (int j = 0; j < LP::NJ; ++j)
+        lds_dma16<NT>(is_v ? rv_w : rk_w, __builtin_amdgcn_readfirstlane(base + LP::lds_off(j)),
+                      is_v ? lp.v[j] : lp.k[j], tile_bytes);
+    };
+    if (stream)
+      go(std::true_type{});
+    else
+      go(std::false_type{});
   };
   NonShared<D, KG> ns;
   ns.L = early_slots ? __builtin_amdgcn_readfirstlane(lenv) : 0;  // the fused append sets it below

@@ -453,7 +453,8 @@ xattn_status xattn_cht_form_batch(xattn_cht* cht, int32_t max_batch, int64_t max
 
 /*
  * MEASUREMENT UTILITY (not part of the attention path): reads `bytes` of
- * device memory at src once, with 16-byte vector loads spread over every CU,
+ * device memory at src once, with 16-byte non-temporal vector loads spread
+ * over every CU (eight in flight per thread; the fastest of the forms tried),
  * and discards the data. Timing it gives the practical HBM read ceiling that
  * the attention kernels' bandwidth figures are read against (xGR page,
  * section 4: the baseline kernel's memory pipeline is reported busy most of
