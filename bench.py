@@ -133,6 +133,78 @@ def measured_traffic(cfg):
     return int(e["fetch_kib"] * 1024 * cal["fetch_factor"] + e["write_kib"] * 1024 * cal["write_factor"])
 
 
+TRAFFIC_WORKLOADS = ("5", "2", "3", "4A", "4B")
+
+
+def collect_traffic(d):
+    """Write profiles/traffic.json from rocprofv3 counter runs under directory
+    d (host only, no GPU): d/copy_fetch and d/copy_write hold FETCH_SIZE and
+    WRITE_SIZE of `bench.py --calibrate-copy 1073741824`; d/fetch_<cfg> and
+    d/write_<cfg> those of `bench.py --config <cfg> --profile-steps 3`, with
+    that run's stdout in d/fetch_<cfg>.log (its JSON line names the layers and
+    the kernel sources). Each was written by
+    rocprofv3 --pmc <COUNTER> --output-format csv -d d/<name> -o p -- python3 bench.py ..."""
+    import csv
+
+    def rows(name, ctr):
+        fn = os.path.join(d, name, "p_counter_collection.csv")
+        rs = [r for r in csv.DictReader(open(fn)) if r["Counter_Name"] == ctr]
+        return sorted(rs, key=lambda r: int(r["Dispatch_Id"]))
+
+    def copy_kib(name, ctr):
+        rs = rows(name, ctr)
+        cp = [r for r in rs if "copy" in r["Kernel_Name"].lower()] or rs[-1:]
+        return float(cp[-1]["Counter_Value"])
+
+    def run_info(name):
+        for line in open(os.path.join(d, name + ".log")):
+            if line.startswith("{") and "profile_steps" in line:
+                return json.loads(line)
+        raise SystemExit(f"collect_traffic: no profile-steps line in {name}.log")
+
+    def per_call(name, ctr, n_layers):
+        rs = rows(name, ctr)
+        first = next(i for i, r in enumerate(rs) if "beam_topk" in r["Kernel_Name"])
+        steps, cur = [], None
+        for r in rs[first:]:
+            if "beam_topk" in r["Kernel_Name"]:
+                cur = []
+                steps.append(cur)
+            else:
+                cur.append(float(r["Counter_Value"]))
+        n_calls = len(steps) * n_layers
+        return sum(map(sum, steps)) / n_calls, len(steps[-1]) // n_layers, n_calls
+
+    cal_bytes = 1073741824
+    fetch_c, write_c = copy_kib("copy_fetch", "FETCH_SIZE"), copy_kib("copy_write", "WRITE_SIZE")
+    cal = dict(bytes=cal_bytes, fetch_kib=round(fetch_c, 3), write_kib=round(write_c, 3),
+               fetch_factor=round(cal_bytes / 1024 / fetch_c, 4), write_factor=round(cal_bytes / 1024 / write_c, 4))
+    out = {"about": ("HBM bytes per xattn_append_decode call (every kernel launch of the call) from rocprofv3 "
+                     "--pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over the call's dispatches), "
+                     "each scaled by the factor the same counter needs for a plain 1 GiB device-to-device copy "
+                     "(bench.py --calibrate-copy 1073741824). Commands: rocprofv3 --pmc FETCH_SIZE (then "
+                     "WRITE_SIZE) --output-format csv -d <dir> -o p -- python3 bench.py --config <cfg> "
+                     "--profile-steps 3; the calls are the dispatches after the first beam selection (3 steps x "
+                     "n_layers calls); written by bench.py --collect-traffic <dir>. kernel_hash identifies the "
+                     "library sources the counts were taken on (bench.py kernel_hash()): the Shared-stage, "
+                     "vector, append and merge kernels and the dispatch."),
+           "copy_calibration": cal, "workloads": {}}
+    for c in TRAFFIC_WORKLOADS:
+        if not os.path.exists(os.path.join(d, f"fetch_{c}")):
+            continue
+        info = run_info(f"fetch_{c}")
+        f, n_disp, n_calls = per_call(f"fetch_{c}", "FETCH_SIZE", info["n_layers"])
+        w, _, _ = per_call(f"write_{c}", "WRITE_SIZE", info["n_layers"])
+        out["workloads"][c] = dict(kernel_hash=info["kernel_hash"], fetch_kib=round(f, 2), write_kib=round(w, 2),
+                                   dispatches_per_call=n_disp, calls=n_calls,
+                                   traffic_bytes=int(f * 1024 * cal["fetch_factor"] + w * 1024 * cal["write_factor"]))
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out["workloads"]))
+
+
 def _spread(xs):
     xs = list(xs)
     return dict(median=round(statistics.median(xs), 5), min=round(min(xs), 5), max=round(max(xs), 5),
@@ -612,7 +684,12 @@ def main():
                     help="only build the workload and run N eager steps (for counter collection), then exit")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from the host instead of one captured step graph")
+    ap.add_argument("--collect-traffic", default=None, metavar="DIR",
+                    help="host only: write profiles/traffic.json from the rocprofv3 counter runs under DIR, then exit")
     args = ap.parse_args()
+    if args.collect_traffic:
+        collect_traffic(args.collect_traffic)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(requests shard across GPUs with no exchange; see the design notes).",

@@ -77,6 +77,7 @@ xattn_status check_dims(const xattn_dims* d) {
     return XATTN_ERR_INVALID_ARG;
   if (d->key_groups < 0 || d->key_groups == 3 || d->key_groups > 4) return XATTN_ERR_INVALID_ARG;
   if (d->key_groups == 4 && d->pipeline_stages == 4) return XATTN_ERR_INVALID_ARG;  // LDS
+  if (d->prompts_disjoint != 0 && d->prompts_disjoint != 1) return XATTN_ERR_INVALID_ARG;
   // The scale must be finite and positive: the kernels take a tile's running
   // maximum as max(q.k) * scale (a negative scale would make it the minimum)
   // and multiply masked scores of -inf by it (0 or inf would give NaN).
@@ -349,6 +350,9 @@ hipError_t run_prefix(const xattn_dims* d, const Plan& p, int mode, const void* 
     a.gen_member = (mode == kModeFixup && kp != nullptr) ? 1 : 0;
     a.stages = p.stages;
     a.key_groups = p.kgroups;
+    // A workgroup alone reads its prompt keys: one row tile, and no other
+    // request's prompt overlaps (the caller's guarantee).
+    a.stream_kv = d->prompts_disjoint != 0 && p.row_tiles == 1;
     a.append = fa ? 1 : 0;
     a.k_new = fa ? static_cast<const uint16_t*>(fa->k_new) : nullptr;
     a.v_new = fa ? static_cast<const uint16_t*>(fa->v_new) : nullptr;

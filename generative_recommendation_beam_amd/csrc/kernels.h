@@ -54,6 +54,7 @@ struct SharedMfmaArgs {
   int gen_member;   // kModeFixup with k_pool: one extra member per group does the Non-Shared tokens
   int stages;       // LDS pipeline stages: 2 or 4
   int key_groups;   // 1, 2 or 4 wave groups splitting each workgroup's keys
+  int stream_kv;    // prompt keys read by this workgroup alone: non-temporal loads
   // Fused cache append (kModeFinal, one member): slot_table is the table
   // read (table_in), the new token of each active beam comes from
   // k_new/v_new, and the launch also writes its pool rows, table_out and

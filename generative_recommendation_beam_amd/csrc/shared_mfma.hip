@@ -384,12 +384,15 @@ __device__ __forceinline__ i32x4_t raw_rsrc_words(const void* base, int num_reco
 // load writes and would wait for every one in flight before each LDS read
 // of the other stage. The walks wait for these loads themselves (vmcnt) and
 // publish them with a barrier. No register is written. NT marks the load
-// non-temporal (chosen per call, outside the unrolled load sequences). Measured on MI355X: for keys that no other
+// non-temporal (chosen per call, outside the unrolled load sequences); the
+// kernel streams a prompt when its workgroup is the keys' only reader (one
+// row tile, prompts of different requests disjoint). Measured on MI355X: for keys that no other
 // workgroup reads (a single row tile) streaming them is faster (64 distinct
 // 4608-token sequences, one decode: 226 -> 201 us); where the row tiles of
 // a (request, kv head) share the keys through L2 it is slower (16 requests
 // of 256 beams over 16384-token prompts: 2026 -> 2153 us), so those keep
-// the default policy.
+// the default policy; so do prompts that several requests alias (16
+// requests on each of 4 shared 4608-token ranges: 147 -> 160 us).
 template <bool NT>
 __device__ __forceinline__ void lds_dma16(i32x4_t rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
   if constexpr (NT)
@@ -836,7 +839,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   // LDS reads.
   const i32x4_t rk_w = raw_rsrc_words(Kg, prompt_bytes);
   const i32x4_t rv_w = raw_rsrc_words(Vg, prompt_bytes);
-  const bool stream = a.row_tiles == 1;  // this workgroup is its keys' only reader
+  const bool stream = a.stream_kv != 0;  // this workgroup is its keys' only reader
   auto issue_part = [&](int t, bool do_k, bool do_v) {
     const uint32_t buf = (uint32_t)(uintptr_t)lsm + (uint32_t)((t % NS) * SBUF + wave * 1024);
     const int pt = t < nsup - 1 ? (t + rot) % (nsup - 1) : t;  // super-tile loaded at step t

@@ -56,7 +56,8 @@ def upload(w: Workload, device="cuda", *, prefix_splits=0, unshared_splits=0,
                            num_slots=w.num_slots, num_prefix_tokens=w.n_ptok, scale=w.scale,
                            prefix_splits=prefix_splits, unshared_splits=unshared_splits,
                            rows_per_block=rows_per_block, pipeline_stages=pipeline_stages,
-                           key_groups=key_groups)
+                           key_groups=key_groups,
+                           prompts_disjoint=xattn.prompts_disjoint(w.prefix_off, w.prefix_len))
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     T = w.T_steps
     act = np.stack([w.active(t) for t in range(T)]) if T else np.zeros((0, w.R), np.uint8)

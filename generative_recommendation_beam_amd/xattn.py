@@ -36,7 +36,8 @@ class Dims(ctypes.Structure):
                 ("num_slots", ctypes.c_int64), ("num_prefix_tokens", ctypes.c_int64),
                 ("scale", ctypes.c_float), ("prefix_splits", ctypes.c_int32),
                 ("unshared_splits", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
-                ("pipeline_stages", ctypes.c_int32), ("key_groups", ctypes.c_int32)]
+                ("pipeline_stages", ctypes.c_int32), ("key_groups", ctypes.c_int32),
+                ("prompts_disjoint", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -178,11 +179,18 @@ def _stream(stream):
 
 def make_dims(*, R, B, Hq, Hkv, D, max_prefix_len, max_unshared_len, dtype, num_slots,
               num_prefix_tokens, scale, prefix_splits=0, unshared_splits=0, rows_per_block=0,
-              pipeline_stages=0, key_groups=0) -> Dims:
+              pipeline_stages=0, key_groups=0, prompts_disjoint=0) -> Dims:
     return Dims(int(R), int(B), int(Hq), int(Hkv), int(D), int(max_prefix_len),
                 int(max_unshared_len), int(dtype), int(num_slots), int(num_prefix_tokens),
                 float(scale), int(prefix_splits), int(unshared_splits), int(rows_per_block),
-                int(pipeline_stages), int(key_groups))
+                int(pipeline_stages), int(key_groups), int(prompts_disjoint))
+
+
+def prompts_disjoint(prefix_off, prefix_len) -> bool:
+    """True when no two requests' prompt ranges [off, off + len) overlap
+    (empty ranges overlap nothing): the guarantee behind the dims hint."""
+    rs = sorted((int(o), int(o) + int(n)) for o, n in zip(prefix_off, prefix_len) if int(n) > 0)
+    return all(a[1] <= b[0] for a, b in zip(rs, rs[1:]))
 
 
 def workspace_size(dims: Dims, which: int) -> int:

@@ -100,6 +100,15 @@ typedef struct {
                                only; else XATTN_ERR_UNSUPPORTED, or
                                XATTN_ERR_INVALID_ARG for 4 stages) take the
                                32-key halves of two 64-key tiles per step */
+  int32_t prompts_disjoint; /* 0 or 1 (else XATTN_ERR_INVALID_ARG). 1: the caller
+                               guarantees that no two requests' prompt ranges
+                               [prefix_off[r], prefix_off[r] + P_r) overlap. A
+                               prompt that one workgroup alone reads (a single
+                               tile of query rows) is then loaded with
+                               non-temporal loads, which stream it past the
+                               caches; with aliased prompts (0) other requests
+                               find it in the caches, so the default policy
+                               stays. A cache hint only: results are identical. */
 } xattn_dims;
 
 /* Launch plan chosen for a dims (introspection for tests and tuning). */

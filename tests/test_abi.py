@@ -75,6 +75,8 @@ def _decode(d, ws=None, nbytes=0, **over):
     (dict(key_groups=4, D=64), xattn.XATTN_ERR_UNSUPPORTED),
     (dict(key_groups=4, rows_per_block=128), xattn.XATTN_ERR_UNSUPPORTED),
     (dict(rows_per_block=96), xattn.XATTN_ERR_INVALID_ARG),
+    (dict(prompts_disjoint=2), xattn.XATTN_ERR_INVALID_ARG),
+    (dict(prompts_disjoint=-1), xattn.XATTN_ERR_INVALID_ARG),
     (dict(max_prefix_len=1 << 23), xattn.XATTN_ERR_UNSUPPORTED),   # prompt bytes reach 2^31
     (dict(max_prefix_len=1 << 22, dtype=xattn.XATTN_F32), xattn.XATTN_ERR_UNSUPPORTED),
 ])
@@ -227,3 +229,15 @@ def test_stream_read_host_checks(L):
     assert L.xattn_stream_read(FAKE + 8, 1024, sink, None) == xattn.XATTN_ERR_INVALID_ARG
     assert L.xattn_stream_read(FAKE, 1000, sink, None) == xattn.XATTN_ERR_INVALID_ARG
     assert L.xattn_stream_read(FAKE, 1024, None, None) == xattn.XATTN_ERR_INVALID_ARG
+
+
+def test_prompts_disjoint_hint():
+    """The upload path sets the cache hint only when no two requests' prompt
+    ranges overlap (empty ranges overlap nothing)."""
+    assert xattn.prompts_disjoint([0, 100, 300], [100, 200, 5])
+    assert xattn.prompts_disjoint([0, 0], [10, 0])          # an empty range
+    assert not xattn.prompts_disjoint([0, 0], [10, 10])     # aliased
+    assert not xattn.prompts_disjoint([0, 50], [100, 100])  # partial overlap
+    assert not xattn.prompts_disjoint([50, 0], [100, 60])   # unsorted, overlapping
+    assert xattn.prompts_disjoint([], [])
+    assert xattn.Dims().prompts_disjoint == 0               # default: no guarantee
