@@ -129,6 +129,63 @@ struct ValuState {
     }
   }
 
+  // A batch of U steps, each over the 4 keys held by the 4 slots: kv[u] /
+  // vv[u] are this lane's D/16 elements of its slot's key and value rows in
+  // step u; step u holds a key for this slot iff u < nvalid. The scores of
+  // the whole batch come first; the reference maximum then moves at most
+  // once per batch (lazily: only when a score passes it by more than 8, in
+  // log2 units, so every weight stays below 2^8), and the weights and value
+  // updates follow as straight-line code.
+  template <int U>
+  __device__ __forceinline__ void update_batch(const KRow<T, EPL>* kv, const float (*vv)[EPL], int nvalid) {
+    float s[U][NG];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) s[u][g] = sizeof(T) == 2 ? q[g].dot(kv[u]) * qscale : q[g].dot(kv[u]);
+    // Steps past nvalid get -inf through a min with a bound chosen apart from
+    // the sums (a select would let the compiler branch around them).
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float bound = u < nvalid ? __builtin_inff() : neg_inf();
+#pragma unroll
+      for (int g = 0; g < NG; ++g) s[u][g] = fminf(slot_sum(s[u][g]), bound);
+    }
+    bool move = false;
+    float mx[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      mx[g] = s[0][g];
+#pragma unroll
+      for (int u = 1; u < U; ++u) mx[g] = fmaxf(mx[g], s[u][g]);
+      move |= mx[g] > m[g] + 8.0f;
+    }
+    if (__any(move)) {  // rare after the first batch
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const bool mv = mx[g] > m[g] + 8.0f;
+        const float mn = mv ? mx[g] : m[g];
+        const float alpha = mv ? exp2_approx(m[g] - mn) : 1.0f;  // m = -inf -> 0
+        l[g] *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+        m[g] = mn;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      // a slot with no key yet keeps m = -inf and only -inf scores: weight 0
+      const float mref = m[g] == neg_inf() ? 0.f : m[g];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = exp2_approx(s[u][g] - mref);
+        l[g] += p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] += p * vv[u][e];
+      }
+    }
+  }
+
   // One step over the 4 keys held by the 4 slots: kv / vv are this lane's
   // D/16 elements of its slot's key and value rows; `valid` is uniform per
   // slot.
@@ -253,8 +310,12 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
         kv[u].load(kb + jj * D);
         Load<T, EPL>::run(vb + jj * D, vv[u]);
       }
+      if constexpr (sizeof(T) == 2) {
+        st.template update_batch<U>(kv, vv, (k1 - j0 - slot_id + 3) / 4);
+      } else {  // fp32 (small prompts): per-step updates, invalid steps skipped
 #pragma unroll
-      for (int u = 0; u < U; ++u) st.update(kv[u], vv[u], j0 + 4 * u + slot_id < k1);
+        for (int u = 0; u < U; ++u) st.update(kv[u], vv[u], j0 + 4 * u + slot_id < k1);
+      }
     }
   }
   if (a.use_gen && (!a.use_prefix || split == 0)) {  // beside a split prompt: in split 0
@@ -283,8 +344,12 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) slot[u] = trow[min(j0 + 4 * U + 4 * u + slot_id, t1 - 1)];
+        if constexpr (sizeof(T) == 2) {
+          st.template update_batch<U>(kv, vv, (t1 - j0 - slot_id + 3) / 4);
+        } else {
 #pragma unroll
-        for (int u = 0; u < U; ++u) st.update(kv[u], vv[u], j0 + 4 * u + slot_id < t1);
+          for (int u = 0; u < U; ++u) st.update(kv[u], vv[u], j0 + 4 * u + slot_id < t1);
+        }
       }
     }
   }
