@@ -114,10 +114,104 @@ struct KRow<float, EPL> {
 template <typename T, int D, int NG>
 struct ValuState {
   static constexpr int EPL = D / 16;
+  // Four bf16 query heads: during the walk the heads are spread over a key
+  // slot's 16 lanes. Lane i of a slot belongs to head group c = (i / 4) % 4
+  // and holds its heads in the order c, c+1, c+2, c+3 (mod 4): q[j] and
+  // acc[j] are head (c + j) & 3. A score's 16-lane sum then reduces all four
+  // heads at once (each level adds the partner's copy of the heads this lane
+  // keeps: 2 + 1 + 2 row operations instead of 4 per head), every lane ends
+  // with the full score of head c, which only it (and its group) turns into
+  // a weight, and the four weights reach every lane by three row rotations.
+  // m[0] / l[0] are head c's; to_absolute() restores the plain layout.
+  static constexpr bool REL = NG == 4 && sizeof(T) == 2;
   KRow<T, EPL> q[NG];  // bf16: as loaded; fp32: pre-scaled by scale_log2
   float qscale;        // applied to each bf16 score (the fp32 q carries it)
   float m[NG], l[NG];
   float acc[NG][EPL];
+
+  // head group of this lane within its key slot
+  __device__ __forceinline__ static int head_group(int lane) { return (lane >> 2) & 3; }
+  // the values of heads c+1, c+2, c+3 from the lanes of those head groups
+  // (lane i reads lane i+4, i+8, i+12 of its 16-lane row)
+  __device__ __forceinline__ static void spread(float x, float* out) {
+    out[0] = x;
+    out[1] = dpp_f32<0x12C>(x);  // row_ror:12 (lane i + 4)
+    out[2] = dpp_f32<0x128>(x);  // row_ror:8  (lane i + 8)
+    out[3] = dpp_f32<0x124>(x);  // row_ror:4  (lane i - 4)
+  }
+
+  // The plain layout after a walk in the head-group layout: m, l and acc per
+  // absolute head in every lane.
+  __device__ __forceinline__ void to_absolute(int lane) {
+    if constexpr (REL) {
+      const int c = head_group(lane);
+      float mr[4], lr[4];
+      spread(m[0], mr);
+      spread(l[0], lr);
+      float ar[4][EPL];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ar[j][e] = acc[j][e];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int j = (g - c) & 3;  // head g sits at relative index j
+        m[g] = j == 0 ? mr[0] : j == 1 ? mr[1] : j == 2 ? mr[2] : mr[3];
+        l[g] = j == 0 ? lr[0] : j == 1 ? lr[1] : j == 2 ? lr[2] : lr[3];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+          acc[g][e] = j == 0 ? ar[0][e] : j == 1 ? ar[1][e] : j == 2 ? ar[2][e] : ar[3][e];
+      }
+    }
+  }
+
+  // Batch update in the head-group layout (see update_batch).
+  template <int U>
+  __device__ __forceinline__ void update_batch_rel(const KRow<T, EPL>* kv, const float (*vv)[EPL], int nvalid) {
+    float sc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float s4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s4[j] = q[j].dot(kv[u]);
+      // lanes i and i-8 (head groups c and c+2): keep heads c, c+1
+      const float t0 = s4[0] + dpp_f32<0x128>(s4[2]);
+      const float t1 = s4[1] + dpp_f32<0x128>(s4[3]);
+      // lane i-4 (group c-1) holds head c as its second: all four groups
+      float x = t0 + dpp_f32<0x124>(t1);
+      x += dpp_f32<0xB1>(x);  // quad_perm [1,0,3,2]
+      x += dpp_f32<0x4E>(x);  // quad_perm [2,3,0,1]
+      sc[u] = fminf(x * qscale, u < nvalid ? __builtin_inff() : neg_inf());
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u]);
+    const bool mv = mx > m[0] + 8.0f;
+    if (__any(mv)) {  // rare after the first batch
+      const float mn = mv ? mx : m[0];
+      const float alpha = mv ? exp2_approx(m[0] - mn) : 1.0f;  // m = -inf -> 0
+      l[0] *= alpha;
+      m[0] = mn;
+      float ar[4];
+      spread(alpha, ar);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] *= ar[j];
+    }
+    const float mref = m[0] == neg_inf() ? 0.f : m[0];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = exp2_approx(sc[u] - mref);
+      l[0] += p;
+      float pr[4];
+      spread(p, pr);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] += pr[j] * vv[u][e];
+    }
+  }
 
   __device__ __forceinline__ void init() {
 #pragma unroll
@@ -280,14 +374,15 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
     const T* qb = static_cast<const T*>(a.q) + ((n * s.Hq) + h * G + g0) * (int64_t)D + dl * EPL;
     st.qscale = s.scale_log2;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
+    for (int j = 0; j < NG; ++j) {
+      const int g = decltype(st)::REL ? (st.head_group(lane) + j) & 3 : j;  // head of q[j]
       if (g < ng)
-        st.q[g].load(qb + (int64_t)g * D);
+        st.q[j].load(qb + (int64_t)g * D);
       else
-        st.q[g].zero();
+        st.q[j].zero();
       if constexpr (sizeof(T) == 4) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) st.q[g].f[e] *= s.scale_log2;
+        for (int e = 0; e < EPL; ++e) st.q[j].f[e] *= s.scale_log2;
       }
     }
   }
@@ -310,7 +405,9 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
         kv[u].load(kb + jj * D);
         Load<T, EPL>::run(vb + jj * D, vv[u]);
       }
-      if constexpr (sizeof(T) == 2) {
+      if constexpr (decltype(st)::REL) {
+        st.template update_batch_rel<U>(kv, vv, (k1 - j0 - slot_id + 3) / 4);
+      } else if constexpr (sizeof(T) == 2) {
         st.template update_batch<U>(kv, vv, (k1 - j0 - slot_id + 3) / 4);
       } else {  // fp32 (small prompts): per-step updates, invalid steps skipped
 #pragma unroll
@@ -344,7 +441,9 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) slot[u] = trow[min(j0 + 4 * U + 4 * u + slot_id, t1 - 1)];
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (decltype(st)::REL) {
+          st.template update_batch_rel<U>(kv, vv, (t1 - j0 - slot_id + 3) / 4);
+        } else if constexpr (sizeof(T) == 2) {
           st.template update_batch<U>(kv, vv, (t1 - j0 - slot_id + 3) / 4);
         } else {
 #pragma unroll
@@ -353,6 +452,7 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
       }
     }
   }
+  st.to_absolute(lane);
   st.combine_slots(lane);
   // The wave (split) that finalizes query head g of the group.
   auto owner = [&](int g) { return (WGM && a.fold_parts > 0) ? g % a.splits : 0; };
