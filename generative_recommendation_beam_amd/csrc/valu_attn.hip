@@ -111,7 +111,7 @@ struct KRow<float, EPL> {
   }
 };
 
-template <typename T, int D, int NG>
+template <typename T, int D, int NG, bool BATCH>
 struct ValuState {
   static constexpr int EPL = D / 16;
   // Four bf16 query heads: during the walk the heads are spread over a key
@@ -123,7 +123,7 @@ struct ValuState {
   // with the full score of head c, which only it (and its group) turns into
   // a weight, and the four weights reach every lane by three row rotations.
   // m[0] / l[0] are head c's; to_absolute() restores the plain layout.
-  static constexpr bool REL = NG == 4 && sizeof(T) == 2;
+  static constexpr bool REL = BATCH && NG == 4 && sizeof(T) == 2;
   KRow<T, EPL> q[NG];  // bf16: as loaded; fp32: pre-scaled by scale_log2
   float qscale;        // applied to each bf16 score (the fp32 q carries it)
   float m[NG], l[NG];
@@ -340,7 +340,7 @@ struct ValuState {
 // WGM: the splits of one (beam, kv head, head group) are the waves of one
 // workgroup (wave w = split w) and are merged there, in split order, into the
 // final output; otherwise kValuWaves consecutive units per workgroup.
-template <typename T, int D, int NG, bool WGM>
+template <typename T, int D, int NG, bool WGM, bool BATCH>
 __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_attn_kernel(
     ValuArgs a, int64_t n_units, int ngroups) {
   constexpr int EPL = D / 16;
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
   const int slot_id = lane >> 4;
   const int dl = lane & 15;
 
-  ValuState<T, D, NG> st;
+  ValuState<T, D, NG, BATCH> st;
   st.init();
   {
     const T* qb = static_cast<const T*>(a.q) + ((n * s.Hq) + h * G + g0) * (int64_t)D + dl * EPL;
@@ -407,9 +407,9 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
       }
       if constexpr (decltype(st)::REL) {
         st.template update_batch_rel<U>(kv, vv, (k1 - j0 - slot_id + 3) / 4);
-      } else if constexpr (sizeof(T) == 2) {
+      } else if constexpr (BATCH) {
         st.template update_batch<U>(kv, vv, (k1 - j0 - slot_id + 3) / 4);
-      } else {  // fp32 (small prompts): per-step updates, invalid steps skipped
+      } else {  // short runs and fp32: per-step updates, invalid steps skipped
 #pragma unroll
         for (int u = 0; u < U; ++u) st.update(kv[u], vv[u], j0 + 4 * u + slot_id < k1);
       }
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
         for (int u = 0; u < U; ++u) slot[u] = trow[min(j0 + 4 * U + 4 * u + slot_id, t1 - 1)];
         if constexpr (decltype(st)::REL) {
           st.template update_batch_rel<U>(kv, vv, (t1 - j0 - slot_id + 3) / 4);
-        } else if constexpr (sizeof(T) == 2) {
+        } else if constexpr (BATCH) {
           st.template update_batch<U>(kv, vv, (t1 - j0 - slot_id + 3) / 4);
         } else {
 #pragma unroll
@@ -564,6 +564,27 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
   }
 }
 
+template <typename T, int D, bool BATCH>
+hipError_t launch_ng(const ValuArgs& a, dim3 grid, dim3 block, int NG, bool wgm, int64_t units, int ngroups,
+                     hipStream_t st) {
+  if (wgm) {
+    switch (NG) {
+      case 1: hipLaunchKernelGGL((valu_attn_kernel<T, D, 1, true, BATCH>), grid, block, 0, st, a, units, ngroups); break;
+      case 2: hipLaunchKernelGGL((valu_attn_kernel<T, D, 2, true, BATCH>), grid, block, 0, st, a, units, ngroups); break;
+      case 4: hipLaunchKernelGGL((valu_attn_kernel<T, D, 4, true, BATCH>), grid, block, 0, st, a, units, ngroups); break;
+      default: hipLaunchKernelGGL((valu_attn_kernel<T, D, 8, true, BATCH>), grid, block, 0, st, a, units, ngroups); break;
+    }
+    return hipGetLastError();
+  }
+  switch (NG) {
+    case 1: hipLaunchKernelGGL((valu_attn_kernel<T, D, 1, false, BATCH>), grid, block, 0, st, a, units, ngroups); break;
+    case 2: hipLaunchKernelGGL((valu_attn_kernel<T, D, 2, false, BATCH>), grid, block, 0, st, a, units, ngroups); break;
+    case 4: hipLaunchKernelGGL((valu_attn_kernel<T, D, 4, false, BATCH>), grid, block, 0, st, a, units, ngroups); break;
+    default: hipLaunchKernelGGL((valu_attn_kernel<T, D, 8, false, BATCH>), grid, block, 0, st, a, units, ngroups); break;
+  }
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const ValuArgs& a, hipStream_t st) {
   const int G = a.s.Hq / a.s.Hkv;
@@ -579,22 +600,12 @@ hipError_t launch_typed(const ValuArgs& a, hipStream_t st) {
   const int wpb = wgm ? a.splits : kValuWaves;
   const int64_t blocks = (units + wpb - 1) / wpb;
   dim3 grid((unsigned)blocks), block(wpb * 64);
-  if (wgm) {
-    switch (NG) {
-      case 1: hipLaunchKernelGGL((valu_attn_kernel<T, D, 1, true>), grid, block, 0, st, a, units, ngroups); break;
-      case 2: hipLaunchKernelGGL((valu_attn_kernel<T, D, 2, true>), grid, block, 0, st, a, units, ngroups); break;
-      case 4: hipLaunchKernelGGL((valu_attn_kernel<T, D, 4, true>), grid, block, 0, st, a, units, ngroups); break;
-      default: hipLaunchKernelGGL((valu_attn_kernel<T, D, 8, true>), grid, block, 0, st, a, units, ngroups); break;
-    }
-    return hipGetLastError();
-  }
-  switch (NG) {
-    case 1: hipLaunchKernelGGL((valu_attn_kernel<T, D, 1, false>), grid, block, 0, st, a, units, ngroups); break;
-    case 2: hipLaunchKernelGGL((valu_attn_kernel<T, D, 2, false>), grid, block, 0, st, a, units, ngroups); break;
-    case 4: hipLaunchKernelGGL((valu_attn_kernel<T, D, 4, false>), grid, block, 0, st, a, units, ngroups); break;
-    default: hipLaunchKernelGGL((valu_attn_kernel<T, D, 8, false>), grid, block, 0, st, a, units, ngroups); break;
-  }
-  return hipGetLastError();
+  // bf16 waves that walk several batches (long generated tails) take the
+  // batched updates; short runs (a few tokens per beam) the per-step ones,
+  // which skip the steps that hold no key. Measured per Non-Shared pass:
+  // 512-token tails 34.2 -> 29.8 us batched, 3-token tails 16.7 -> 19.7 us.
+  if (sizeof(T) == 2 && a.chunk >= 64) return launch_ng<T, D, true>(a, grid, block, NG, wgm, units, ngroups, st);
+  return launch_ng<T, D, false>(a, grid, block, NG, wgm, units, ngroups, st);
 }
 
 }  // namespace
