@@ -165,9 +165,16 @@ struct ValuState {
     }
   }
 
-  // Batch update in the head-group layout (see update_batch).
+  // Batch update in the head-group layout (see update_batch). The value
+  // rows stay as loaded (two bf16 elements per dword), and the weights go
+  // in pairs of steps: the two steps' weights of a head are rounded to bf16
+  // and packed, and one bf16 dot product per output element adds both
+  // steps' weighted values (products exact, sums in fp32), after the two
+  // steps' elements are paired up by byte permutes. The running sum adds
+  // the rounded weights, the ones the values are weighted with.
   template <int U>
-  __device__ __forceinline__ void update_batch_rel(const KRow<T, EPL>* kv, const float (*vv)[EPL], int nvalid) {
+  __device__ __forceinline__ void update_batch_rel(const KRow<T, EPL>* kv, const KRow<T, EPL>* vr, int nvalid) {
+    static_assert(U % 2 == 0, "steps go in pairs");
     float sc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -201,15 +208,25 @@ struct ValuState {
     }
     const float mref = m[0] == neg_inf() ? 0.f : m[0];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float p = exp2_approx(sc[u] - mref);
-      l[0] += p;
+    for (int u = 0; u < U; u += 2) {
+      const bf16x2_t pk{(__bf16)exp2_approx(sc[u] - mref), (__bf16)exp2_approx(sc[u + 1] - mref)};
+      const uint32_t pb = __builtin_bit_cast(uint32_t, pk);
+      l[0] += __uint_as_float(pb << 16) + __uint_as_float(pb & 0xffff0000u);
       float pr[4];
-      spread(p, pr);
+      spread(__uint_as_float(pb), pr);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int i = 0; i < EPL / 2; ++i) {
+        // element 2i of steps u and u+1, then element 2i+1 of both
+        const uint32_t ev = __builtin_amdgcn_perm(vr[u + 1].w[i], vr[u].w[i], 0x05040100u);
+        const uint32_t od = __builtin_amdgcn_perm(vr[u + 1].w[i], vr[u].w[i], 0x07060302u);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[j][e] += pr[j] * vv[u][e];
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2_t pj = __builtin_bit_cast(bf16x2_t, pr[j]);
+          acc[j][2 * i] = __builtin_amdgcn_fdot2_f32_bf16(pj, __builtin_bit_cast(bf16x2_t, ev), acc[j][2 * i], false);
+          acc[j][2 * i + 1] =
+              __builtin_amdgcn_fdot2_f32_bf16(pj, __builtin_bit_cast(bf16x2_t, od), acc[j][2 * i + 1], false);
+        }
+      }
     }
   }
 
@@ -398,6 +415,17 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
     const T* vb = static_cast<const T*>(a.v_shared) + ((int64_t)h * s.n_ptok + a.prefix_off[r]) * D + dl * EPL;
     for (int j0 = k0; j0 < k1; j0 += 4 * U) {
       KRow<T, EPL> kv[U];
+      if constexpr (decltype(st)::REL) {  // value rows as loaded
+        KRow<T, EPL> vr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {  // keys past k1 read row k1-1 and are skipped
+          const int64_t jj = min(j0 + 4 * u + slot_id, k1 - 1);
+          kv[u].load(kb + jj * D);
+          vr[u].load(vb + jj * D);
+        }
+        st.template update_batch_rel<U>(kv, vr, (k1 - j0 - slot_id + 3) / 4);
+        continue;
+      }
       float vv[U][EPL];
 #pragma unroll
       for (int u = 0; u < U; ++u) {  // keys past k1 read row k1-1 and are skipped
@@ -405,9 +433,7 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
         kv[u].load(kb + jj * D);
         Load<T, EPL>::run(vb + jj * D, vv[u]);
       }
-      if constexpr (decltype(st)::REL) {
-        st.template update_batch_rel<U>(kv, vv, (k1 - j0 - slot_id + 3) / 4);
-      } else if constexpr (BATCH) {
+      if constexpr (BATCH) {
         st.template update_batch<U>(kv, vv, (k1 - j0 - slot_id + 3) / 4);
       } else {  // short runs and fp32: per-step updates, invalid steps skipped
 #pragma unroll
@@ -433,6 +459,18 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
       for (int u = 0; u < U; ++u) slot[u] = trow[min(t0 + 4 * u + slot_id, t1 - 1)];
       for (int j0 = t0; j0 < t1; j0 += 4 * U) {
         KRow<T, EPL> kv[U];
+        if constexpr (decltype(st)::REL) {  // value rows as loaded
+          KRow<T, EPL> vr[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            kv[u].load(kp + slot[u] * tok_stride);
+            vr[u].load(vp + slot[u] * tok_stride);
+          }
+#pragma unroll
+          for (int u = 0; u < U; ++u) slot[u] = trow[min(j0 + 4 * U + 4 * u + slot_id, t1 - 1)];
+          st.template update_batch_rel<U>(kv, vr, (t1 - j0 - slot_id + 3) / 4);
+          continue;
+        }
         float vv[U][EPL];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -441,9 +479,7 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) slot[u] = trow[min(j0 + 4 * U + 4 * u + slot_id, t1 - 1)];
-        if constexpr (decltype(st)::REL) {
-          st.template update_batch_rel<U>(kv, vv, (t1 - j0 - slot_id + 3) / 4);
-        } else if constexpr (BATCH) {
+        if constexpr (BATCH) {
           st.template update_batch<U>(kv, vv, (t1 - j0 - slot_id + 3) / 4);
         } else {
 #pragma unroll
