@@ -75,6 +75,16 @@ CASES = {
                              dict(unshared_splits=8, prefix_splits=2), False),
     "long_fold_2splits_d64": (dict(R=2, B=2, Hq=4, Hkv=1, D=64, prefix_len=[300, 0], unshared_len=[33, 20]),
                               dict(unshared_splits=2), False),
+    # tails of 64 tokens or more per Non-Shared split: the vector kernel's
+    # batched updates, with the four heads of G = 4 spread over a key slot's
+    # lanes (head dims 128 and 64) and the plain batches for G = 8, 6
+    # (one masked head group), 2 and 1; partial last batches throughout
+    "batch_g4": (dict(R=2, B=3, Hq=8, Hkv=2, D=128, prefix_len=[400, 130], unshared_len=[150, 77]), {}, False),
+    "batch_g4_d64": (dict(R=2, B=2, Hq=4, Hkv=1, D=64, prefix_len=[300, 0], unshared_len=[100, 65]), {}, False),
+    "batch_g8": (dict(R=1, B=4, Hq=16, Hkv=2, D=128, prefix_len=[500], unshared_len=[130]), {}, False),
+    "batch_g6": (dict(R=1, B=3, Hq=12, Hkv=2, D=128, prefix_len=[256], unshared_len=[90]), {}, False),
+    "batch_g2": (dict(R=2, B=3, Hq=4, Hkv=2, D=128, prefix_len=[200, 64], unshared_len=[96, 70]), {}, False),
+    "batch_g1": (dict(R=1, B=4, Hq=2, Hkv=2, D=64, prefix_len=[128], unshared_len=[80]), {}, False),
     "fallback_splits": (dict(R=2, B=12, Hq=8, Hkv=2, D=128, prefix_len=[640, 200], unshared_len=[3, 2]),
                         dict(prefix_splits=3), False),
     "fallback_f32": (dict(R=2, B=4, Hq=4, Hkv=1, D=64, prefix_len=[256, 100], unshared_len=[2, 3],
