@@ -383,16 +383,16 @@ __device__ __forceinline__ i32x4_t raw_rsrc_words(const void* base, int num_reco
 // assembly: the compiler's wait insertion cannot tell which LDS range such a
 // load writes and would wait for every one in flight before each LDS read
 // of the other stage. The walks wait for these loads themselves (vmcnt) and
-// publish them with a barrier. No register is written. NT marks the load
-// non-temporal (chosen per call, outside the unrolled load sequences); the
-// kernel streams a prompt when its workgroup is the keys' only reader (one
-// row tile, prompts of different requests disjoint). Measured on MI355X: for keys that no other
-// workgroup reads (a single row tile) streaming them is faster (64 distinct
-// 4608-token sequences, one decode: 226 -> 201 us); where the row tiles of
-// a (request, kv head) share the keys through L2 it is slower (16 requests
-// of 256 beams over 16384-token prompts: 2026 -> 2153 us), so those keep
-// the default policy; so do prompts that several requests alias (16
-// requests on each of 4 shared 4608-token ranges: 147 -> 160 us).
+// publish them with a barrier. No register is written.
+// NT marks the load non-temporal (chosen per call, outside the unrolled load
+// sequences). The kernel streams a prompt when its workgroup is the keys'
+// only reader: one row tile, and prompts of different requests disjoint.
+// Measured on MI355X: streaming such keys is faster (64 distinct
+// 4608-token sequences, one decode: 226 -> 201 us); where the row tiles of a
+// (request, kv head) share the keys through L2 it is slower (16 requests of
+// 256 beams over 16384-token prompts: 2026 -> 2153 us), and so it is for
+// prompts that several requests alias (16 requests on each of 4 shared
+// 4608-token ranges: 147 -> 160 us); those keep the default policy.
 template <bool NT>
 __device__ __forceinline__ void lds_dma16(i32x4_t rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
   if constexpr (NT)

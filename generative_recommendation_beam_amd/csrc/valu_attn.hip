@@ -600,25 +600,25 @@ __global__ __launch_bounds__(WGM ? kValuWgMax * 64 : kValuWaves * 64) void valu_
   }
 }
 
+template <typename T, int D, int NG, bool BATCH>
+hipError_t launch_one(const ValuArgs& a, dim3 grid, dim3 block, bool wgm, int64_t units, int ngroups,
+                      hipStream_t st) {
+  if (wgm)
+    hipLaunchKernelGGL((valu_attn_kernel<T, D, NG, true, BATCH>), grid, block, 0, st, a, units, ngroups);
+  else
+    hipLaunchKernelGGL((valu_attn_kernel<T, D, NG, false, BATCH>), grid, block, 0, st, a, units, ngroups);
+  return hipGetLastError();
+}
+
 template <typename T, int D, bool BATCH>
 hipError_t launch_ng(const ValuArgs& a, dim3 grid, dim3 block, int NG, bool wgm, int64_t units, int ngroups,
                      hipStream_t st) {
-  if (wgm) {
-    switch (NG) {
-      case 1: hipLaunchKernelGGL((valu_attn_kernel<T, D, 1, true, BATCH>), grid, block, 0, st, a, units, ngroups); break;
-      case 2: hipLaunchKernelGGL((valu_attn_kernel<T, D, 2, true, BATCH>), grid, block, 0, st, a, units, ngroups); break;
-      case 4: hipLaunchKernelGGL((valu_attn_kernel<T, D, 4, true, BATCH>), grid, block, 0, st, a, units, ngroups); break;
-      default: hipLaunchKernelGGL((valu_attn_kernel<T, D, 8, true, BATCH>), grid, block, 0, st, a, units, ngroups); break;
-    }
-    return hipGetLastError();
-  }
   switch (NG) {
-    case 1: hipLaunchKernelGGL((valu_attn_kernel<T, D, 1, false, BATCH>), grid, block, 0, st, a, units, ngroups); break;
-    case 2: hipLaunchKernelGGL((valu_attn_kernel<T, D, 2, false, BATCH>), grid, block, 0, st, a, units, ngroups); break;
-    case 4: hipLaunchKernelGGL((valu_attn_kernel<T, D, 4, false, BATCH>), grid, block, 0, st, a, units, ngroups); break;
-    default: hipLaunchKernelGGL((valu_attn_kernel<T, D, 8, false, BATCH>), grid, block, 0, st, a, units, ngroups); break;
+    case 1: return launch_one<T, D, 1, BATCH>(a, grid, block, wgm, units, ngroups, st);
+    case 2: return launch_one<T, D, 2, BATCH>(a, grid, block, wgm, units, ngroups, st);
+    case 4: return launch_one<T, D, 4, BATCH>(a, grid, block, wgm, units, ngroups, st);
+    default: return launch_one<T, D, 8, BATCH>(a, grid, block, wgm, units, ngroups, st);
   }
-  return hipGetLastError();
 }
 
 template <typename T, int D>
@@ -639,8 +639,11 @@ hipError_t launch_typed(const ValuArgs& a, hipStream_t st) {
   // bf16 waves that walk several batches (long generated tails) take the
   // batched updates; short runs (a few tokens per beam) the per-step ones,
   // which skip the steps that hold no key. Measured per Non-Shared pass:
-  // 512-token tails 34.2 -> 29.8 us batched, 3-token tails 16.7 -> 19.7 us.
-  if (sizeof(T) == 2 && a.chunk >= 64) return launch_ng<T, D, true>(a, grid, block, NG, wgm, units, ngroups, st);
+  // batched, 512-token tails took 29.8 instead of 34.2 us, but 3-token tails
+  // 19.7 instead of 16.7 us.
+  if constexpr (sizeof(T) == 2) {
+    if (a.chunk >= 64) return launch_ng<T, D, true>(a, grid, block, NG, wgm, units, ngroups, st);
+  }
   return launch_ng<T, D, false>(a, grid, block, NG, wgm, units, ngroups, st);
 }
 
