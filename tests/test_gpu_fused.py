@@ -183,3 +183,31 @@ def test_append_decode_rejects_in_place_tables():
                             slot_base=d.slot_base, active=None, k_pool=d.k_pool, v_pool=d.v_pool,
                             table_in=d.table, table_out=d.table, unshared_len=d.unshared_len, o=o, lse=lse,
                             workspace=ws if nb else None, workspace_bytes=nb)
+
+
+@pytest.mark.parametrize("shape", [
+    # single-beam requests (one 32-row tile per (request, kv head)), and a
+    # request of 16 beams x 4 heads (one 64-row tile), each with a long tail
+    dict(R=4, B=1, Hq=8, Hkv=2, D=128, prefix_len=[700, 512, 90, 300], unshared_len=[3, 2, 1, 3]),
+    dict(R=2, B=16, Hq=8, Hkv=2, D=128, prefix_len=[1100, 600], unshared_len=[40, 33]),
+])
+def test_disjoint_prompt_hint_changes_no_bit(shape):
+    """prompts_disjoint only chooses the prompt loads' cache policy: the same
+    call with the hint set (non-temporal loads where a workgroup alone reads
+    its prompt) and cleared gives the same bits."""
+    w = make_workload("hint", seed_key=(321, shape["B"]), parent_dist="uniform", **shape)
+    outs = []
+    for hint in (1, 0):
+        d = dv.upload(w)
+        assert d.dims.prompts_disjoint == 1  # distinct prompt ranges
+        d.dims.prompts_disjoint = hint
+        plan = xattn.get_plan(d.dims, 2)
+        assert plan["mfma"] == 1 and plan["row_tiles"] == 1, plan
+        dv.build_cache(d)
+        o, lse, ws, nb = dv.alloc_outputs(d, 2)
+        dv.decode(d, o, lse, ws, nb)
+        torch.cuda.synchronize()
+        outs.append((_np(o)[:d.rows].copy(), _np(lse)[:d.rows].copy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    O, L = oa.attention(w)
+    compare(outs[0][0].reshape(O.shape), O, outs[0][1].reshape(L.shape), L, "bf16", "disjoint prompt hint")
