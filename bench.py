@@ -302,27 +302,33 @@ def _ev():
 
 
 def time_steps(s, K, warmup, repeats):
-    """K timed steps after `warmup` untimed ones, bracketed by synchronizes;
-    per-step events give the median and spread; `repeats` more timed runs of
-    K steps give the run-to-run spread."""
+    """K timed steps after `warmup` untimed ones, bracketed by synchronizes,
+    with one event pair around the whole run (events between the steps add
+    their own gaps); then K more steps with an event pair around each step
+    (and each call, eagerly) give the per-step median and spread, and
+    `repeats` more timed runs of K steps the run-to-run spread."""
     import torch
     for _ in range(warmup):
         s.one_step()
     torch.cuda.synchronize()
-    per_step = [(_ev(), _ev()) for _ in range(K)]
-    call_evs = [[(_ev(), _ev()) for _ in s.layers] for _ in range(K)] if s.graphs is None else None
     start, end = _ev(), _ev()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for k in range(K):
-        per_step[k][0].record()
-        s.one_step(None if call_evs is None else call_evs[k])
-        per_step[k][1].record()
+        s.one_step()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
+    per_step = [(_ev(), _ev()) for _ in range(K)]
+    call_evs = [[(_ev(), _ev()) for _ in s.layers] for _ in range(K)] if s.graphs is None else None
+    torch.cuda.synchronize()
+    for k in range(K):
+        per_step[k][0].record()
+        s.one_step(None if call_evs is None else call_evs[k])
+        per_step[k][1].record()
+    torch.cuda.synchronize()
     step_ms = [a.elapsed_time(b) for a, b in per_step]
     reps = []
     for _ in range(repeats):
