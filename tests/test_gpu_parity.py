@@ -117,17 +117,20 @@ KG_CASES = ["ragged_small_bf16", "mfma_multi_tile", "d64_bf16", "g8_bf16", "g16_
             "no_gen_bf16", "long_gen_bf16"]
 
 
-@pytest.mark.parametrize("name", KG_CASES)
-@pytest.mark.parametrize("rows,ps,stages,kg", [(64, 0, 2, 2), (128, 0, 2, 2), (32, 0, 2, 2), (64, 3, 2, 2),
-                                               (64, 0, 4, 2), (128, 0, 4, 2), (32, 0, 4, 2), (64, 3, 4, 2),
-                                               (64, 0, 2, 4), (32, 0, 2, 4), (64, 3, 2, 4)])
+KG_PLANS = [(64, 0, 2, 2), (128, 0, 2, 2), (32, 0, 2, 2), (64, 3, 2, 2),
+            (64, 0, 4, 2), (128, 0, 4, 2), (32, 0, 4, 2), (64, 3, 4, 2),
+            (64, 0, 2, 4), (32, 0, 2, 4), (64, 3, 2, 4)]
+# Four key groups exist for head dim 128 only; the ABI's rejection of the
+# others (XATTN_ERR_UNSUPPORTED) is checked in test_abi.py.
+KG_RUNS = [(n,) + p for n in KG_CASES for p in KG_PLANS if p[3] != 4 or CASES[n]["D"] == 128]
+
+
+@pytest.mark.parametrize("name,rows,ps,stages,kg", KG_RUNS)
 def test_decode_key_groups(name, rows, ps, stages, kg):
     """Wave groups per workgroup split the keys of the same rows: two groups
     on alternate 64-key tiles (2 stages) or on the two halves of every tile
     (4 stages); four groups on the halves of two tiles a step. Prompts here
     end inside any group's share, or leave some groups none."""
-    if kg == 4 and CASES[name]["D"] != 128:
-        pytest.skip("four key groups: head dim 128 only")
     w = make_workload(name, seed_key=(305, rows, ps, kg, zlib.crc32(name.encode()) % 1000), **CASES[name])
     d, o, lse = run_decode(w, rows_per_block=rows, key_groups=kg, prefix_splits=ps, pipeline_stages=stages)
     plan = xattn.get_plan(d.dims, 2)
@@ -205,11 +208,16 @@ def test_vector_late_score_jump_f32_prompt():
 @pytest.mark.parametrize("kg", [0, 2])
 def test_shared_stage_matches_oracle(name, ps, kg):
     """Shared stage alone; single-beam bf16 prompts run on the MFMA kernel
-    too (a 32-row tile), with and without key groups and prompt splits."""
-    if kg and CASES[name].get("dtype") == "f32":
-        pytest.skip("fp32 prompts run on the vector kernel, which has no key groups")
+    too (a 32-row tile), with and without key groups and prompt splits.
+    fp32 prompts run on the vector kernel, which takes no key groups: the
+    forced value is ignored there."""
     w = make_workload(name, seed_key=(302, ps), **CASES[name])
     d = dv.upload(w, prefix_splits=ps, key_groups=kg)
+    plan = xattn.get_plan(d.dims, 0)
+    if CASES[name].get("dtype") == "f32":
+        assert plan["mfma"] == 0 and plan["key_groups"] == 0, plan
+    else:
+        assert plan["mfma"] == 1 and plan["key_groups"] == (kg or plan["key_groups"]), plan
     o, lse, ws, nb = dv.alloc_outputs(d, 0)
     dv.shared_stage(d, o, lse, ws, nb)
     torch.cuda.synchronize()
