@@ -118,11 +118,13 @@ def kernel_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(cfg):
+TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def measured_traffic(cfg, path=TRAFFIC_PATH):
     """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     counts, each scaled by the same counter's reading for a plain copy of known
     size; None if absent or taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
@@ -136,8 +138,8 @@ def measured_traffic(cfg):
 TRAFFIC_WORKLOADS = ("5", "2", "3", "4A", "4B")
 
 
-def collect_traffic(d):
-    """Write profiles/traffic.json from rocprofv3 counter runs under directory
+def collect_traffic(d, path=TRAFFIC_PATH):
+    """Write `path` (profiles/traffic.json) from rocprofv3 counter runs under directory
     d (host only, no GPU): d/copy_fetch and d/copy_write hold FETCH_SIZE and
     WRITE_SIZE of `bench.py --calibrate-copy 1073741824`; d/fetch_<cfg> and
     d/write_<cfg> those of `bench.py --config <cfg> --profile-steps 3`, with
@@ -198,7 +200,6 @@ def collect_traffic(d):
         out["workloads"][c] = dict(kernel_hash=info["kernel_hash"], fetch_kib=round(f, 2), write_kib=round(w, 2),
                                    dispatches_per_call=n_disp, calls=n_calls,
                                    traffic_bytes=int(f * 1024 * cal["fetch_factor"] + w * 1024 * cal["write_factor"]))
-    path = os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
