@@ -302,15 +302,22 @@ def _ev():
     return torch.cuda.Event(enable_timing=True)
 
 
-def time_steps(s, K, warmup, repeats):
-    """K timed steps after `warmup` untimed ones, bracketed by synchronizes,
+def time_steps(s, K, warmup, repeats, min_warm_s=0.0):
+    """K timed steps after `warmup` untimed ones (more, until `min_warm_s`
+    seconds of them have run: a workload measured right after another one
+    finds the clocks where that one left them), bracketed by synchronizes,
     with one event pair around the whole run (events between the steps add
     their own gaps); then K more steps with an event pair around each step
     (and each call, eagerly) give the per-step median and spread, and
     `repeats` more timed runs of K steps the run-to-run spread."""
     import torch
-    for _ in range(warmup):
+    tw = time.perf_counter()
+    n_warm = 0
+    while n_warm < warmup or time.perf_counter() - tw < min_warm_s:
         s.one_step()
+        n_warm += 1
+        if n_warm >= warmup:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     start, end = _ev(), _ev()
     torch.cuda.synchronize()
@@ -344,7 +351,8 @@ def time_steps(s, K, warmup, repeats):
     call_us = None
     if call_evs is not None:
         call_us = [a.elapsed_time(b) * 1e3 for evs in call_evs for a, b in evs]
-    return dict(ms_total=ms_total, wall=wall, step_ms=step_ms, repeat_ms_per_step=reps, eager_call_us=call_us)
+    return dict(ms_total=ms_total, wall=wall, step_ms=step_ms, repeat_ms_per_step=reps, eager_call_us=call_us,
+                warmup_steps=n_warm)
 
 
 def time_graph(g, K, before=None):
@@ -562,7 +570,7 @@ def batch_former_timing():
                 note="host C++ through ctypes (the per-call Python overhead included)")
 
 
-def measure(cfg, args, *, paged_rounds):
+def measure(cfg, args, *, paged_rounds, min_warm_s=0.0):
     """Every GPU figure of one workload: the timed steps (value), the
     dominant kernel's roofline, the separate calls and the comparison."""
     import numpy as np
@@ -571,7 +579,7 @@ def measure(cfg, args, *, paged_rounds):
     s = Setup(cfg, n_layers, args)
     w0, K = s.w0, args.steps
     print(f"[{cfg}] timing {K} steps of {n_layers} layers ...", file=sys.stderr, flush=True)
-    st = time_steps(s, K, args.warmup, args.repeats)
+    st = time_steps(s, K, args.warmup, args.repeats, min_warm_s)
     ms_per_step = st["ms_total"] / K
     value = w0.N_b * n_layers / (ms_per_step / 1e3)
     restore = lambda: s.ulen_all.copy_(s.ulen0)  # the same append every launch
@@ -638,6 +646,7 @@ def measure(cfg, args, *, paged_rounds):
         "ms_per_step": round(ms_per_step, 5),
         "step_ms_spread": _spread(st["step_ms"]),
         "repeat_ms_per_step": [round(x, 5) for x in st["repeat_ms_per_step"]],
+        "warmup_steps": st["warmup_steps"],
         "wall_s_timed": round(st["wall"], 4),
         "config": {"workload": WORKLOAD_NAMES[str(cfg)], "n_layers": n_layers, "beams_per_call": w0.N_b,
                    "step": "beam selection (%d x %d x %d pool -> %d beams per request), then "
@@ -755,7 +764,7 @@ def main():
     }
     result.update(head)
     for c in extras:
-        ex = measure(c, args, paged_rounds=0 if args.no_paged else min(args.steps, 20))
+        ex = measure(c, args, paged_rounds=0 if args.no_paged else min(args.steps, 20), min_warm_s=0.05)
         result[f"config_{c}"] = ex
     if not args.no_stream:
         result["hbm_stream_read"] = stream_bandwidth()
