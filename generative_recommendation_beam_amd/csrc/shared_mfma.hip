@@ -1123,6 +1123,22 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
         constexpr int S = decltype(stage_c)::value;
         const char* buf = smem + S * SBUF;
         const bool next = t + 1 < nfull, next2 = t + 2 < nfull;  // uniform
+        {
+          // Issue priority falls as the walk advances (3 until half the tiles
+          // are done, then 2, 1 and 0 past three quarters and seven eighths):
+          // of the two workgroups sharing a SIMD, the one behind is issued
+          // first and catches up, so both leave the CU closer together
+          // instead of the younger one finishing alone at half the
+          // throughput. Measured on MI355X: 16 requests of 256 beams over
+          // 16384-token prompts 1987 -> 1970 us per call, 4 requests of 512
+          // beams over 2048-token prompts (one round of workgroups)
+          // 94.6 -> 91.7 us.
+          const int rem = nfull - t;  // uniform
+          if (rem * 2 > nfull) __builtin_amdgcn_s_setprio(3);
+          else if (rem * 4 > nfull) __builtin_amdgcn_s_setprio(2);
+          else if (rem * 8 > nfull) __builtin_amdgcn_s_setprio(1);
+          else __builtin_amdgcn_s_setprio(0);
+        }
         pipe_s_rescale_probs<D>(buf, kbase, 1, qf, sn, sc, c, m_run, pf, l_part, rescale, mxp);
         mxp = pipe_pv_then_max<D>(buf, vbase, 0, pf, oacc, sn);
         sc = sn;
@@ -1151,6 +1167,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
         body(I1{});
       }
       if (t < nfull) body(I0{});
+      __builtin_amdgcn_s_setprio(0);  // the default again for the rest of the kernel
     }
     // Without two full tiles, or for the partial last tile: the masked step
     // (its loads requested now when the walk left them out).
