@@ -1196,6 +1196,13 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   wait_vmem();
   // This wave's tile of super-tile `it` sits at stage (it % NS), slot kg.
   for (int it = 0; it + 1 < nsup; ++it) {  // full super-tiles
+    if constexpr (NW == 4) {  // two workgroups per CU: as in the pipelined walk
+      const int rem = nsup - it;  // uniform
+      if (rem * 2 > nsup) __builtin_amdgcn_s_setprio(3);
+      else if (rem * 4 > nsup) __builtin_amdgcn_s_setprio(2);
+      else if (rem * 8 > nsup) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     advance(it);
     if constexpr (HALF)
       half_tile_step<D, false>(smem + (it % NS) * SBUF + (kg >> 1) * (TPS - 1) * TG::BUFB, kbase, vbase, qf,
@@ -1209,6 +1216,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
       tok_after = issued - 1;
     }
   }
+  if constexpr (NW == 4) __builtin_amdgcn_s_setprio(0);
   if (NPF > 0 && nsup <= 1) fetch_tokens();
   if (nsup > 0) {  // the last super-tile: this wave's tile may be partial or empty
     const int it = nsup - 1;
