@@ -32,7 +32,7 @@ lengths are restored (events cannot be recorded inside a captured graph on
 the runtime PyTorch ships). Also reported: per-step median and spread,
 repeated timed runs, the unfused path (Shared stage + Non-Shared stage +
 Merge) and the append alone, the Non-Shared stage's own HBM fraction, the
-box's streaming-read bandwidth, the PagedAttention-style comparison, and the
+GPU's streaming-read bandwidth, the PagedAttention-style comparison, and the
 fp64 oracle timed on the host's cores (a child process).
 """
 from __future__ import annotations
@@ -707,8 +707,8 @@ def main():
         collect_traffic(args.collect_traffic)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(requests shard across GPUs with no exchange; see the design notes).",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(whole requests would be placed per GPU, with no exchange inside attention).",
               file=sys.stderr)
         sys.exit(2)
 
