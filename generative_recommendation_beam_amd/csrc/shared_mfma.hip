@@ -1196,7 +1196,10 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void shared_mfma_kernel(S
   wait_vmem();
   // This wave's tile of super-tile `it` sits at stage (it % NS), slot kg.
   for (int it = 0; it + 1 < nsup; ++it) {  // full super-tiles
-    if constexpr (NW == 4) {  // two workgroups per CU: as in the pipelined walk
+    // Issue priority falls with the walk's progress, as in the pipelined walk.
+    // Measured on MI355X (64 single-beam requests on 4 shared 4608-token
+    // prompts): 151.4 -> 146.0 us per call; distinct prompts unchanged.
+    if constexpr (NW == 4) {
       const int rem = nsup - it;  // uniform
       if (rem * 2 > nsup) __builtin_amdgcn_s_setprio(3);
       else if (rem * 4 > nsup) __builtin_amdgcn_s_setprio(2);
